@@ -1,0 +1,275 @@
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one pass over every stage of the path, each on its own synthetic
+seeded workload with inputs already resident in HBM:
+  * causal GQA prefill, B=1, Hq=32, Hkv=8, N=4096, d=128, bf16 (the headline
+    workload: ``value`` is its TFLOP/s),
+  * kv_append of 4 new tokens + paged 4-token decode, B=32, 16-token blocks,
+    cached lengths uniform in [1024, 16384],
+  * split-KV decode of 1 token against 16 contiguous 32768-token caches.
+Each stage is timed with HIP events recorded on the stream the library
+launches on; the long-context prefill (N=32768) and the fp32 single-head case
+are timed in their own loops after the steps. FLOPs count visible
+(query, key) pairs x 4d; decode bytes count each visible K/V row once.
+Prints ONE JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+METRIC = "prefill attention TFLOP/s and decode KV-read GB/s, % of MI355X peak"
+
+
+def causal_pairs(nq, nk, q_offset=0):
+    """Visible (row, key) pairs of a causal nq x nk mask, closed form."""
+    tot = 0
+    # row i sees min(nk, max(0, i + q_offset + 1)) keys
+    for i in range(nq):
+        tot += min(nk, max(0, i + q_offset + 1))
+    return tot
+
+
+def prefill_flops(B, Hq, N, d, causal=True):
+    pairs = causal_pairs(N, N) if causal else N * N
+    return 4.0 * d * B * Hq * pairs
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--long-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="time only the 4k prefill stage (for profiling runs)")
+    return ap.parse_args()
+
+
+class StageTimer:
+    """Per-stage HIP events on one stream; durations summed over the timed steps."""
+
+    def __init__(self, torch, stream, names):
+        self.torch = torch
+        self.stream = stream
+        self.names = names
+        self.pairs = {n: [] for n in names}
+
+    def run(self, name, fn, record=True):
+        if not record:
+            fn()
+            return
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record(self.stream)
+        fn()
+        ev1.record(self.stream)
+        self.pairs[name].append((ev0, ev1))
+
+    def mean_ms(self, name):
+        ps = self.pairs[name]
+        return sum(a.elapsed_time(b) for a, b in ps) / len(ps)
+
+
+def cpu_baseline(q, k, v, heads):
+    """Time the fp64 oracle on `heads` of the 4k causal prefill (all rows)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the visible cores
+        threads = os.cpu_count()
+    qc = q.cpu()
+    kc = k.cpu()
+    vc = v.cpu()
+    d = q.shape[-1]
+    G = q.shape[1] // k.shape[1]
+    t0 = time.perf_counter()
+    for hq in heads:
+        oracle.attention_rows(qc[0, hq], np.arange(q.shape[2]), kc[0, hq // G], vc[0, hq // G],
+                              1.0 / math.sqrt(d), True)
+    dt = time.perf_counter() - t0
+    flops = prefill_flops(1, len(heads), q.shape[2], d)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(heads)} of 32 heads, all 4096 rows, of the causal GQA 4k prefill "
+                      f"(fp64 numpy, {dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import exact_tiled_attention_flashattention_amd as eta
+    from exact_tiled_attention_flashattention_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    eta.library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}; building inputs", file=sys.stderr,
+          flush=True)
+
+    # ---- inputs (seeded, generated on the device) ---------------------------------
+    q2, k2, v2 = inputs.workload_inputs("causal_gqa_prefill_4k", dev)
+    o2 = torch.empty_like(q2)
+    l2 = torch.empty(q2.shape[:3], dtype=torch.float32, device=dev)
+    w4 = inputs.WORKLOADS["splitkv_decode_32k"]
+    q4, kc4, vc4, sl4 = inputs.workload_inputs("splitkv_decode_32k", dev)
+    o4 = torch.empty_like(q4)
+    l4 = torch.empty((w4["B"], w4["Hq"], 1), dtype=torch.float32, device=dev)
+    ws4 = torch.empty(eta.attn_decode_workspace_bytes(w4["B"], w4["Hq"], w4["Hkv"], 1, w4["d"],
+                                                      w4["seq_len"]), dtype=torch.uint8, device=dev)
+    w5 = inputs.WORKLOADS["paged_decode_q4"]
+    p5 = inputs.workload_inputs("paged_decode_q4", dev)
+    L5 = p5["block_table"].shape[1] * 16
+    o5 = torch.empty_like(p5["q"])
+    l5 = torch.empty((w5["B"], w5["Hq"], 4), dtype=torch.float32, device=dev)
+    ws5 = torch.empty(eta.attn_decode_workspace_bytes(w5["B"], w5["Hq"], w5["Hkv"], 4, w5["d"], L5),
+                      dtype=torch.uint8, device=dev)
+    seq5 = [int(x) for x in p5["seq_lens"].cpu()]
+    torch.cuda.synchronize()
+
+    def prefill4k():
+        eta.attn_prefill(q2, k2, v2, causal=True, out=o2, lse=l2)
+
+    def append5():
+        eta.kv_append(p5["k_new"], p5["v_new"], p5["k_pool"], p5["v_pool"], p5["cache_lens"],
+                      block_table=p5["block_table"])
+
+    def decode5():
+        eta.attn_decode_paged(p5["q"], p5["k_pool"], p5["v_pool"], p5["seq_lens"],
+                              block_table=p5["block_table"], causal=True, workspace=ws5, out=o5,
+                              lse=l5)
+
+    def decode4():
+        eta.attn_decode_paged(q4, kc4, vc4, sl4, causal=True, workspace=ws4, out=o4, lse=l4)
+
+    stages = [("prefill_4k", prefill4k)]
+    if not args.only_prefill:
+        stages += [("kv_append_q4", append5), ("paged_decode_q4", decode5),
+                   ("splitkv_decode_32k", decode4)]
+    timer = StageTimer(torch, stream, [n for n, _ in stages])
+
+    for _ in range(args.warmup):
+        for n, fn in stages:
+            timer.run(n, fn, record=False)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for n, fn in stages:
+            timer.run(n, fn)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    flops2 = prefill_flops(1, 32, 4096, 128)
+    ms2 = timer.mean_ms("prefill_4k")
+    tflops2 = flops2 / (ms2 * 1e-3) / 1e12
+    result_workloads = {
+        "causal_gqa_prefill_4k": {"ms": round(ms2, 5), "TFLOP/s": round(tflops2, 2),
+                                  "frac_of_peak": round(tflops2 / PEAK_BF16_TFLOPS, 4),
+                                  "flops": flops2},
+    }
+    if not args.only_prefill:
+        bytes4 = 2 * 2 * w4["Hkv"] * w4["d"] * w4["B"] * w4["seq_len"]
+        ms4 = timer.mean_ms("splitkv_decode_32k")
+        bytes5 = 2 * 2 * w5["Hkv"] * w5["d"] * sum(seq5)
+        ms5 = timer.mean_ms("paged_decode_q4")
+        msa = timer.mean_ms("kv_append_q4")
+        result_workloads["splitkv_decode_32k"] = {
+            "ms": round(ms4, 5), "GB/s": round(bytes4 / (ms4 * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(bytes4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "kv_bytes": bytes4}
+        result_workloads["paged_decode_q4"] = {
+            "ms": round(ms5, 5), "GB/s": round(bytes5 / (ms5 * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(bytes5 / (ms5 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "kv_bytes": bytes5, "kv_append_ms": round(msa, 5)}
+
+        # long-context prefill and the fp32 single-head case, in their own loops
+        print("[bench] long-context prefill", file=sys.stderr, flush=True)
+        del kc4, vc4
+        torch.cuda.empty_cache()
+        q3, k3, v3 = inputs.workload_inputs("causal_gqa_prefill_32k", dev)
+        o3 = torch.empty_like(q3)
+        l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
+        t3 = StageTimer(torch, stream, ["p"])
+        eta.attn_prefill(q3, k3, v3, causal=True, out=o3, lse=l3)
+        for _ in range(max(1, args.long_steps)):
+            t3.run("p", lambda: eta.attn_prefill(q3, k3, v3, causal=True, out=o3, lse=l3))
+        torch.cuda.synchronize()
+        ms3 = t3.mean_ms("p")
+        flops3 = prefill_flops(1, 32, 32768, 128)
+        result_workloads["causal_gqa_prefill_32k"] = {
+            "ms": round(ms3, 4), "TFLOP/s": round(flops3 / (ms3 * 1e-3) / 1e12, 2),
+            "frac_of_peak": round(flops3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "flops": flops3}
+        q1, k1, v1 = inputs.workload_inputs("single_head_f32", dev)
+        t1 = StageTimer(torch, stream, ["p"])
+        for _ in range(10):
+            eta.attn_prefill(q1, k1, v1, causal=False)
+        for _ in range(50):
+            t1.run("p", lambda: eta.attn_prefill(q1, k1, v1, causal=False))
+        torch.cuda.synchronize()
+        result_workloads["single_head_f32"] = {"us": round(t1.mean_ms("p") * 1e3, 2)}
+
+    roofline = {"bound": "mfma", "achieved": round(tflops2, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops2 / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "kernel": "prefill_bf16_kernel<128, causal>",
+                "per_launch": f"{flops2:.6g} FLOP (visible pairs x 4d) per launch"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(q2, k2, v2, heads=list(range(8)))
+        cpu["host"] = platform.processor() or platform.machine()
+        cpu["host_cpus"] = os.cpu_count()
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops2, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal_gqa_prefill_4k", "B": 1, "Hq": 32, "Hkv": 8, "N": 4096,
+                   "d": 128, "causal": True,
+                   "step": [n for n, _ in stages]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": result_workloads,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,238 @@
-"""MI355X-native exact tiled attention (placeholder until the binding lands)."""
+"""MI355X-native exact tiled attention: Python binding of libattn.so.
+
+Thin ctypes marshalling over the C ABI in ``include/attn.h``: shape, dtype
+and device checks, output allocation through torch, and the call. Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+If ``libattn.so`` has not been built (``__graft_entry__.build()`` or
+``python -m exact_tiled_attention_flashattention_amd.build``), every call
+raises.
+
+Entry points (same names as the C ABI):
+    attn_prefill(q, k, v, scale=None, causal=False, q_offset=0)      -> (o, lse)
+    attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, ...) -> (o, lse)
+    kv_append(k_new, v_new, k_cache, v_cache, cache_lens, block_table=None, ...)
+    attn_gather_paged(cache, seq_lens, block_table, max_seq_len)     -> out
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK = 0
+ATTN_EINVAL = -1
+ATTN_EUNSUPPORTED = -2
+ATTN_EWORKSPACE = -3
+ATTN_EHIP = -4
+ATTN_F32 = 0
+ATTN_BF16 = 1
+BLOCK_TOKENS = 16
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _load().attn_strerror(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+            "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
+    lib.attn_prefill.restype = I
+    lib.attn_decode_paged.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I, I, I,
+                                      P, SZ, P]
+    lib.attn_decode_paged.restype = I
+    lib.attn_decode_num_splits.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_decode_num_splits.restype = I
+    lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_decode_workspace_bytes.restype = SZ
+    lib.kv_append.argtypes = [P, P, P, P, P, I, I, P, I, I, I, I, I, I, P]
+    lib.kv_append.restype = I
+    lib.attn_gather_paged.argtypes = [P, P, I, I, P, P, I, I, I, I, I, P]
+    lib.attn_gather_paged.restype = I
+    lib.attn_strerror.argtypes = [I]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes handle (raises if libattn.so is missing)."""
+    return _load()
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status, where):
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def attn_prefill(q, k, v, scale=None, causal=False, q_offset=0, out=None, lse=None,
+                 want_lse=True):
+    """Prefill. q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d] -> o [B,Hq,Nq,d], lse [B,Hq,Nq] f32."""
+    lib = _load()
+    _need_gpu(q, k, v)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _need_gpu(out, lse)
+    st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq,
+                          Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(q_offset),
+                          _stream(q.device))
+    _check(st, "attn_prefill")
+    return out, lse
+
+
+def attn_decode_num_splits(B, Hq, Hkv, Nq, d, max_seq_len, num_splits=0):
+    st = _load().attn_decode_num_splits(B, Hq, Hkv, Nq, d, max_seq_len, num_splits)
+    _check(min(st, 0), "attn_decode_num_splits")
+    return st
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, max_seq_len, num_splits=0):
+    return int(_load().attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, max_seq_len, num_splits))
+
+
+def _cache_geometry(k_cache, block_table, max_seq_len):
+    if block_table is None:
+        cap = k_cache.shape[1]
+        return (cap if max_seq_len is None else int(max_seq_len)), 0, 0
+    mb = block_table.shape[1]
+    cap = mb * BLOCK_TOKENS
+    return (cap if max_seq_len is None else int(max_seq_len)), mb, k_cache.shape[0]
+
+
+def attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=None, causal=True,
+                      max_seq_len=None, num_splits=0, workspace=None, out=None, lse=None,
+                      want_lse=True):
+    """Decode. q [B,Nq,Hq,d]; caches [P,16,Hkv,d] (paged) or [B,L,Hkv,d] (contiguous);
+    seq_lens [B] int32 (keys incl. the Nq new ones) -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
+    lib = _load()
+    _need_gpu(q, k_cache, v_cache, seq_lens, block_table)
+    B, Nq, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must share a shape with head dim d")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B, max_blocks]")
+        if k_cache.shape[1] != BLOCK_TOKENS:
+            raise ValueError("a paged cache is [num_blocks, 16, Hkv, d]")
+    elif k_cache.shape[0] != B:
+        raise ValueError("a contiguous cache is [B, max_len, Hkv, d]")
+    L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, L, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _need_gpu(workspace, out, lse)
+    st = lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), mb,
+                               nblocks, _ptr(seq_lens), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq,
+                               Hkv, Nq, d, float(scale), int(bool(causal)), L, int(num_splits),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(q.device))
+    _check(st, "attn_decode_paged")
+    return out, lse
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, cache_lens, block_table=None, max_seq_len=None):
+    """Write k_new/v_new [B,Nnew,Hkv,d] at positions cache_lens[b] + r (in place)."""
+    lib = _load()
+    _need_gpu(k_new, v_new, k_cache, v_cache, cache_lens, block_table)
+    B, Nnew, Hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or k_cache.shape[2:] != (Hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between new rows and cache")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("new rows and cache must share one dtype")
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    st = lib.kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                       mb, nblocks, _ptr(cache_lens), _dtype_code(k_new), B, Hkv, Nnew, d, L,
+                       _stream(k_new.device))
+    _check(st, "kv_append")
+
+
+def attn_gather_paged(cache, seq_lens, block_table=None, max_seq_len=None, out=None):
+    """Gather each sequence's first seq_lens[b] rows into out [B, max_seq_len, Hkv, d]."""
+    lib = _load()
+    _need_gpu(cache, seq_lens, block_table)
+    B = seq_lens.shape[0]
+    Hkv, d = cache.shape[2], cache.shape[3]
+    L, mb, nblocks = _cache_geometry(cache, block_table, max_seq_len)
+    if out is None:
+        out = torch.zeros((B, L, Hkv, d), dtype=cache.dtype, device=cache.device)
+    _need_gpu(out)
+    st = lib.attn_gather_paged(_ptr(cache), _ptr(block_table), mb, nblocks, _ptr(seq_lens),
+                               _ptr(out), _dtype_code(cache), B, Hkv, d, L, _stream(cache.device))
+    _check(st, "attn_gather_paged")
+    return out
+
+
+__all__ = [
+    "attn_prefill",
+    "attn_decode_paged",
+    "attn_decode_num_splits",
+    "attn_decode_workspace_bytes",
+    "kv_append",
+    "attn_gather_paged",
+    "library",
+    "AttnError",
+    "LIB_PATH",
+]

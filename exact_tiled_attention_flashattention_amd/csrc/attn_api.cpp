@@ -1,0 +1,235 @@
+// Host side of the C ABI declared in include/attn.h: argument validation,
+// dispatch on dtype / head dim / causal, split sizing, launch on the caller's
+// stream. Nothing here allocates, frees or synchronises; every error is
+// detected before the first launch.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kSplitKeyAlign = 32;      // keys per step of the decode kernel
+constexpr long long kTargetWaves = 8192; // enough independent waves to fill 256 CUs several times
+constexpr int kMinChunk = 256;
+constexpr int kMaxChunk = 8192;
+constexpr int kMaxRows = 16;            // G*Nq rows per decode wave (one 16-wide MFMA)
+
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
+
+struct SplitPlan {
+  int splits;
+  int chunk;
+};
+
+// Keys per chunk: a multiple of 32; by default sized so that B*Hkv*splits
+// waves number about kTargetWaves, within [kMinChunk, kMaxChunk].
+SplitPlan plan_splits(int B, int Hkv, int max_seq_len, int num_splits) {
+  SplitPlan sp;
+  const long long L = max_seq_len > 0 ? max_seq_len : 1;
+  long long chunk;
+  if (num_splits > 0) {
+    chunk = (L + num_splits - 1) / num_splits;
+  } else {
+    const long long work = (long long)B * Hkv * L;
+    chunk = (work + kTargetWaves - 1) / kTargetWaves;
+    if (chunk < kMinChunk) chunk = kMinChunk;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+  }
+  chunk = (chunk + kSplitKeyAlign - 1) / kSplitKeyAlign * kSplitKeyAlign;
+  if (chunk < kSplitKeyAlign) chunk = kSplitKeyAlign;
+  sp.chunk = (int)chunk;
+  sp.splits = (int)((L + chunk - 1) / chunk);
+  return sp;
+}
+
+int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
+                       int num_splits) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || max_seq_len < 0 || num_splits < 0)
+    return ATTN_EINVAL;
+  if (Hq % Hkv != 0) return ATTN_EINVAL;
+  if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (!head_dim_ok(d)) return ATTN_EUNSUPPORTED;
+  if ((long long)(Hq / Hkv) * Nq > kMaxRows) return ATTN_EUNSUPPORTED;
+  return ATTN_OK;
+}
+
+size_t workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, const SplitPlan& sp) {
+  const long long M = (long long)(Hq / Hkv) * Nq;
+  const long long rows = (long long)B * Hkv * sp.splits * M;
+  const long long o_bytes = (rows * d * 4 + 255) / 256 * 256;
+  return (size_t)(o_bytes + rows * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_EINVAL: return "invalid argument";
+    case ATTN_EUNSUPPORTED: return "unsupported dtype, head dim or group size";
+    case ATTN_EWORKSPACE: return "workspace missing or too small";
+    case ATTN_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 int q_offset, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0) return ATTN_EINVAL;
+  if (Hq % Hkv != 0) return ATTN_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  if (q_offset > (1 << 30) || q_offset < -(1 << 30)) return ATTN_EINVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (!head_dim_ok(d)) return ATTN_EUNSUPPORTED;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (q == nullptr || o == nullptr) return ATTN_EINVAL;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return ATTN_EINVAL;
+  if (misaligned16(q) || misaligned16(o) || misaligned16(k) || misaligned16(v) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ATTN_EINVAL;
+  attn::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, q_offset};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, s)
+                                      : attn::launch_prefill_f32(a, s));
+}
+
+int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
+                           int num_splits) {
+  const int st = check_decode_shape(ATTN_BF16, B, Hq, Hkv, Nq, d, max_seq_len, num_splits);
+  if (st != ATTN_OK) return st;
+  return plan_splits(B, Hkv, max_seq_len, num_splits).splits;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
+                                   int num_splits) {
+  if (check_decode_shape(ATTN_BF16, B, Hq, Hkv, Nq, d, max_seq_len, num_splits) != ATTN_OK)
+    return 0;
+  return workspace_bytes(B, Hq, Hkv, Nq, d, plan_splits(B, Hkv, max_seq_len, num_splits));
+}
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                      const int32_t* seq_lens, void* o, float* lse, int dtype, int B, int Hq,
+                      int Hkv, int Nq, int d, float scale, int causal, int max_seq_len,
+                      int num_splits, void* workspace, size_t workspace_bytes_given,
+                      void* stream) {
+  const int st = check_decode_shape(dtype, B, Hq, Hkv, Nq, d, max_seq_len, num_splits);
+  if (st != ATTN_OK) return st;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  if (block_table != nullptr && (max_blocks_per_seq <= 0 || num_blocks < 0)) return ATTN_EINVAL;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (q == nullptr || o == nullptr || seq_lens == nullptr) return ATTN_EINVAL;
+  if (max_seq_len > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_EINVAL;
+  if (misaligned16(q) || misaligned16(o) || misaligned16(k_cache) || misaligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return ATTN_EINVAL;
+  const SplitPlan sp = plan_splits(B, Hkv, max_seq_len, num_splits);
+  const size_t need = workspace_bytes(B, Hq, Hkv, Nq, d, sp);
+  if (workspace == nullptr || misaligned16(workspace) || workspace_bytes_given < need)
+    return ATTN_EWORKSPACE;
+  const long long rows = (long long)B * Hkv * sp.splits * (Hq / Hkv) * Nq;
+  const long long o_bytes = (rows * d * 4 + 255) / 256 * 256;
+  attn::DecodeArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.max_blocks = block_table ? max_blocks_per_seq : 0;
+  a.num_blocks = block_table ? num_blocks : 0;
+  a.seq_lens = seq_lens;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.d = d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.max_seq_len = max_seq_len;
+  a.num_splits = sp.splits;
+  a.chunk = sp.chunk;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  return status_of(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+static int check_copy(const void* a, const void* b, const int32_t* block_table,
+                      int max_blocks_per_seq, int num_blocks, const int32_t* lens, int dtype,
+                      int B, int Hkv, int n, int d, int max_seq_len) {
+  if (B < 0 || Hkv <= 0 || n < 0 || max_seq_len < 0) return ATTN_EINVAL;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (!head_dim_ok(d)) return ATTN_EUNSUPPORTED;
+  if (block_table != nullptr && (max_blocks_per_seq <= 0 || num_blocks < 0)) return ATTN_EINVAL;
+  if (B == 0 || n == 0) return ATTN_OK;
+  if (a == nullptr || b == nullptr || lens == nullptr) return ATTN_EINVAL;
+  if (misaligned16(a) || misaligned16(b) || (reinterpret_cast<uintptr_t>(lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return ATTN_EINVAL;
+  return 1;  // proceed
+}
+
+int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+              const int32_t* cache_lens, int dtype, int B, int Hkv, int Nnew, int d,
+              int max_seq_len, void* stream) {
+  int st = check_copy(k_new, v_new, block_table, max_blocks_per_seq, num_blocks, cache_lens,
+                      dtype, B, Hkv, Nnew, d, max_seq_len);
+  if (st <= 0) return st;
+  if (max_seq_len == 0) return ATTN_OK;  // no position can be written
+  if (k_cache == nullptr || v_cache == nullptr || misaligned16(k_cache) || misaligned16(v_cache))
+    return ATTN_EINVAL;
+  attn::CacheCopyArgs a;
+  a.src_k = k_new;
+  a.src_v = v_new;
+  a.dst_k = k_cache;
+  a.dst_v = v_cache;
+  a.block_table = block_table;
+  a.max_blocks = block_table ? max_blocks_per_seq : 0;
+  a.num_blocks = block_table ? num_blocks : 0;
+  a.lens = cache_lens;
+  a.elem_bytes = dtype == ATTN_BF16 ? 2 : 4;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.Nnew = Nnew;
+  a.d = d;
+  a.max_seq_len = max_seq_len;
+  return status_of(attn::launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_gather_paged(const void* cache, const int32_t* block_table, int max_blocks_per_seq,
+                      int num_blocks, const int32_t* seq_lens, void* out, int dtype, int B,
+                      int Hkv, int d, int max_seq_len, void* stream) {
+  int st = check_copy(cache, out, block_table, max_blocks_per_seq, num_blocks, seq_lens, dtype,
+                      B, Hkv, max_seq_len, d, max_seq_len);
+  if (st <= 0) return st;
+  attn::CacheCopyArgs a;
+  a.src_k = cache;
+  a.src_v = nullptr;
+  a.dst_k = out;
+  a.dst_v = nullptr;
+  a.block_table = block_table;
+  a.max_blocks = block_table ? max_blocks_per_seq : 0;
+  a.num_blocks = block_table ? num_blocks : 0;
+  a.lens = seq_lens;
+  a.elem_bytes = dtype == ATTN_BF16 ? 2 : 4;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.Nnew = 0;
+  a.d = d;
+  a.max_seq_len = max_seq_len;
+  return status_of(attn::launch_gather(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,296 @@
+// Split-KV decode against a paged or contiguous cache, bf16, gfx950.
+//
+// Method: Flash-Decoding ("[BEE-30062] FlashAttention 與高效注意力核心",
+// Background): during decode the batch and the query length are small, so
+// the keys of each sequence are cut into chunks processed in parallel; each
+// chunk yields a partial softmax result that a second pass merges in a
+// numerically stable way. The cache is either the (batch, seqlen, n_kv_heads,
+// head_dim) layout of "為長上下文推論啟用 FlashDecoding" or the same rows cut
+// into 16-token blocks behind a page table ("Phase 07 · 12", section "Paged
+// attention"). Query row i of sequence b sits at position seq_len - Nq + i
+// ("Effizienz", "Der wichtige Maskenfehler beim Cache").
+//
+// Mapping onto CDNA4. Decode reads every K/V byte once and does ~4 flops per
+// byte, so it is bound by HBM bandwidth; the kernel's job is to keep enough
+// bytes in flight and to spend little issue bandwidth per byte.
+//   * One wave per (sequence, K/V head, key chunk). All G·Nq query rows that
+//     share the K/V head (G = Hq/Hkv query heads × Nq new tokens, at most 16)
+//     are the 16 columns of v_mfma_f32_16x16x32_bf16, so every K/V byte is
+//     loaded from HBM once and used by all of them.
+//   * Sᵀ = K·Qᵀ: K rows come straight from global memory into the A operand
+//     (lane = key, 8 consecutive d per lane), Qᵀ sits in registers.
+//   * Oᵀ = Vᵀ·Pᵀ: V rows are loaded 16 bytes per lane (8 consecutive d of one
+//     key, a whole 256-byte row per 16 lanes) and transposed in registers with
+//     byte permutes into the A operand, one MFMA per d residue mod 8. Pᵀ is
+//     the Sᵀ accumulator packed to bf16.
+//   * Every 16-key half of a 32-key step is one cache block; its address is
+//     looked up once per step. Keys past seq_len or in invalid blocks are
+//     never loaded (zeros) and are masked, so stale or NaN cache contents
+//     cannot leak into the result.
+//   * Partial results (normalised O and base-2 LSE per chunk and row) go to
+//     the caller's workspace; the combine kernel merges them with weights
+//     exp2(LSE_s - max_s LSE_s) and writes O (bf16) and the natural-log LSE.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+struct DecodeParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  CacheView cv;
+  const int32_t* seq_lens;
+  __bf16* o;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int B, Hq, Hkv, Nq, G, M, S, chunk;
+  float c;  // scale * log2(e)
+  int causal;
+};
+
+__device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) {
+  // (low 16 bits of x) | (low 16 bits of y) << 16
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {
+  // (high 16 bits of x) | (high 16 bits of y) << 16
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
+  constexpr int NC = D / 32;  // MFMAs per 16 keys for Sᵀ (32 d each)
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= p.B * p.Hkv * p.S) return;
+  const int split = wid % p.S;
+  const int bk = wid / p.S;
+  const int b = bk / p.Hkv;
+  const int kvh = bk % p.Hkv;
+  const int r16 = lane & 15;  // query row (Sᵀ/Oᵀ column) of this lane
+  const int g = lane >> 4;    // lane group 0..3
+
+  const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
+  const int kb0 = split * p.chunk;
+  const int ke = min(n, kb0 + p.chunk);
+  float* po = p.part_o + ((long long)bk * p.S + split) * p.M * D;
+  float* pl = p.part_lse + ((long long)bk * p.S + split) * p.M;
+
+  // rows r = qi * G + h, r < M
+  const bool row_ok = r16 < p.M;
+  const int qi = row_ok ? r16 / p.G : 0;
+  int limit = ke;  // keys of this chunk visible to the row: [kb0, limit)
+  if (p.causal) limit = min(limit, n - p.Nq + qi + 1);
+
+  // Qᵀ as the B operand: lane holds row r16, d = 32*c + 8*g + j
+  bf16x8_t qf[NC];
+  {
+    const int h = row_ok ? r16 % p.G : 0;
+    const __bf16* qp =
+        p.q + (((long long)b * p.Nq + qi) * p.Hq + (long long)kvh * p.G + h) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qp + 32 * c) : bf16x8_t{};
+  }
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{};
+  float m_run = neg_inf();
+  float l_run = 0.f;
+
+  const long long rstride = (long long)p.cv.hkv * D;  // elements between consecutive tokens
+  const __bf16* kbase = p.k + (long long)kvh * D;
+  const __bf16* vbase = p.v + (long long)kvh * D;
+  const bool v_lane = (8 * r16) < D;  // lanes whose 8-wide d chunk exists
+
+  for (int k0 = kb0; k0 < ke; k0 += 32) {
+    long long row0[2];
+    row0[0] = cache_row(p.cv, b, k0);
+    row0[1] = cache_row(p.cv, b, k0 + 16);
+
+    // ---- loads: K into the A operand, V as 8 consecutive d of 8 keys -------
+    bf16x8_t kf[2][NC];
+    u32x4_t vv[2][4];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int key = k0 + 16 * h2 + r16;
+      const bool ok = row0[h2] >= 0 && key < ke;
+      const __bf16* kp = kbase + row0[h2] + (long long)r16 * rstride + 8 * g;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kf[h2][c] = ok ? *reinterpret_cast<const bf16x8_t*>(kp + 32 * c) : bf16x8_t{};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int vk = 4 * g + jj;
+        const bool vok = v_lane && row0[h2] >= 0 && (k0 + 16 * h2 + vk) < ke;
+        vv[h2][jj] = vok ? *reinterpret_cast<const u32x4_t*>(vbase + row0[h2] +
+                                                             (long long)vk * rstride + 8 * r16)
+                         : u32x4_t{0, 0, 0, 0};
+      }
+    }
+
+    // ---- Sᵀ[key][row] ---------------------------------------------------------
+    f32x4_t s[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      s[h2] = f32x4_t{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h2][c], qf[c], s[h2], 0, 0, 0);
+    }
+    float mx = neg_inf();
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 16 * h2 + 4 * g + i;
+        const bool vis = row0[h2] >= 0 && key < limit;
+        if (!vis) s[h2][i] = neg_inf();
+        mx = fmaxf(mx, s[h2][i]);
+      }
+    mx = max_across_rows16(mx);
+    mx = max_across_halves(mx);
+    const float m_new = fmaxf(m_run, mx * p.c);
+    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h2][i], p.c, -m_use));
+        s[h2][i] = e;
+        rs += e;
+      }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+
+    // ---- Oᵀ += Vᵀ Pᵀ: key slot j of lane group g is key 16*(j/4) + 4*g + j%4 ----
+    const bf16x4_t p0 = __builtin_convertvector(s[0], bf16x4_t);
+    const bf16x4_t p1 = __builtin_convertvector(s[1], bf16x4_t);
+    const bf16x8_t pb = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // dword e of each V chunk holds d = 8*r16 + 2e, 2e+1
+      u32x4_t lo, hi;
+      lo[0] = perm_lo(vv[0][0][e], vv[0][1][e]);
+      lo[1] = perm_lo(vv[0][2][e], vv[0][3][e]);
+      lo[2] = perm_lo(vv[1][0][e], vv[1][1][e]);
+      lo[3] = perm_lo(vv[1][2][e], vv[1][3][e]);
+      hi[0] = perm_hi(vv[0][0][e], vv[0][1][e]);
+      hi[1] = perm_hi(vv[0][2][e], vv[0][3][e]);
+      hi[2] = perm_hi(vv[1][0][e], vv[1][1][e]);
+      hi[3] = perm_hi(vv[1][2][e], vv[1][3][e]);
+      acc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), pb,
+                                                           acc[2 * e], 0, 0, 0);
+      acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
+                                                               pb, acc[2 * e + 1], 0, 0, 0);
+    }
+  }
+
+  // ---- partial result of this chunk --------------------------------------------
+  float l_tot = sum_across_rows16(l_run);
+  l_tot = sum_across_halves(l_tot);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    // Oᵀ element (m = 4*g + i, c) is d = 8*m + c = 32*g + 8*i + c
+    if (32 * g < D) {
+      float* dst = po + (long long)r16 * D + 32 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4_t a = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
+        f32x4_t bq = {acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv};
+        *reinterpret_cast<f32x4_t*>(dst + 8 * i) = a;
+        *reinterpret_cast<f32x4_t*>(dst + 8 * i + 4) = bq;
+      }
+    }
+    if (g == 0) pl[r16] = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : neg_inf();
+  }
+}
+
+// One workgroup of D threads per (sequence, K/V head, query row).
+template <int D>
+__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
+  const int d = threadIdx.x;
+  const int r = blockIdx.x % p.M;
+  const int bk = blockIdx.x / p.M;
+  const int b = bk / p.Hkv;
+  const int kvh = bk % p.Hkv;
+  const int qi = r / p.G;
+  const int hq = kvh * p.G + r % p.G;
+  const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
+  const int used = min(p.S, (n + p.chunk - 1) / p.chunk);
+  const float* pl = p.part_lse + (long long)bk * p.S * p.M + r;
+  const float* po = p.part_o + ((long long)bk * p.S * p.M + r) * D + d;
+
+  float mx = neg_inf();
+  for (int s = 0; s < used; ++s) mx = fmaxf(mx, pl[(long long)s * p.M]);
+  float tot = 0.f, acc = 0.f;
+  if (mx != neg_inf()) {
+    for (int s = 0; s < used; ++s) {
+      const float ls = pl[(long long)s * p.M];
+      const float w = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
+      tot += w;
+      acc = __builtin_fmaf(w, po[(long long)s * p.M * D], acc);
+    }
+  }
+  const float out = tot > 0.f ? acc / tot : 0.f;
+  p.o[(((long long)b * p.Nq + qi) * p.Hq + hq) * D + d] = (__bf16)out;
+  if (d == 0 && p.lse != nullptr)
+    p.lse[((long long)b * p.Hq + hq) * p.Nq + qi] =
+        tot > 0.f ? (mx + __builtin_amdgcn_logf(tot)) * kLn2 : neg_inf();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+  DecodeParams pp;
+  pp.q = static_cast<const __bf16*>(a.q);
+  pp.k = static_cast<const __bf16*>(a.k_cache);
+  pp.v = static_cast<const __bf16*>(a.v_cache);
+  pp.cv.table = a.block_table;
+  pp.cv.max_blocks = a.max_blocks;
+  pp.cv.num_blocks = a.num_blocks;
+  pp.cv.max_len = a.max_seq_len;
+  pp.cv.hkv = a.Hkv;
+  pp.cv.d = a.d;
+  pp.seq_lens = a.seq_lens;
+  pp.o = static_cast<__bf16*>(a.o);
+  pp.lse = a.lse;
+  pp.part_o = a.part_o;
+  pp.part_lse = a.part_lse;
+  pp.B = a.B;
+  pp.Hq = a.Hq;
+  pp.Hkv = a.Hkv;
+  pp.Nq = a.Nq;
+  pp.G = a.Hq / a.Hkv;
+  pp.M = pp.G * a.Nq;
+  pp.S = a.num_splits;
+  pp.chunk = a.chunk;
+  pp.c = a.scale * kLog2e;
+  pp.causal = a.causal;
+  const long long waves = (long long)a.B * a.Hkv * pp.S;
+  if (waves <= 0) return hipSuccess;
+  const long long blocks = (waves + 3) / 4;
+  const long long cblocks = (long long)a.B * a.Hkv * pp.M;
+  if (blocks > 0x7fffffffLL || cblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.d == 128) {
+    hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((int)blocks), dim3(256), 0, s, pp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int)cblocks), dim3(128), 0, s, pp);
+  } else {
+    hipLaunchKernelGGL(decode_partial_kernel<64>, dim3((int)blocks), dim3(256), 0, s, pp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int)cblocks), dim3(64), 0, s, pp);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

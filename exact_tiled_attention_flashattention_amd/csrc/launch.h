@@ -1,0 +1,64 @@
+// Internal host-side launchers (one per kernel family). The C ABI in attn.h
+// validates every argument before calling these; they only size grids and
+// enqueue on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  int q_offset;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  int max_blocks;
+  int num_blocks;
+  const int32_t* seq_lens;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, d;
+  float scale;
+  int causal;
+  int max_seq_len;
+  int num_splits;
+  int chunk;  // keys per split, a multiple of 32
+  float* part_o;    // [B*Hkv*num_splits*M, d]
+  float* part_lse;  // [B*Hkv*num_splits*M]
+};
+
+struct CacheCopyArgs {
+  const void* src_k;  // append: new rows; gather: the cache
+  const void* src_v;  // append only
+  void* dst_k;        // append: the cache; gather: out
+  void* dst_v;        // append only
+  const int32_t* block_table;
+  int max_blocks;
+  int num_blocks;
+  const int32_t* lens;  // append: cache_lens; gather: seq_lens
+  int elem_bytes;
+  int B, Hkv, Nnew, d;
+  int max_seq_len;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_kv_append(const CacheCopyArgs& a, hipStream_t s);
+hipError_t launch_gather(const CacheCopyArgs& a, hipStream_t s);
+
+}  // namespace attn

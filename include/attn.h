@@ -1,0 +1,167 @@
+/*
+ * attn.h — C ABI of libattn.so: exact tiled attention for AMD MI355X (gfx950).
+ *
+ * What it computes. O = softmax(scale · Q Kᵀ + mask) V for every query row,
+ * exactly (no approximation), tile by tile with a running maximum and running
+ * sum per row, so the score matrix never exists in device memory:
+ *   - "Phase 07 · 12: KV cache, Flash Attention and inference optimisation"
+ *     (AI Engineering from Scratch), section "tiling trick" (standard
+ *     attention S = Q Kᵀ, P = softmax(S), O = P V, and the tiled loop that
+ *     writes each output tile once) and "Build it, step 2" (running max/sum);
+ *   - "大模型面试笔记——Attention篇" (juejin), §2 (online safe softmax, one fused
+ *     kernel) and §4 (the 1/√h scaling, here the explicit `scale`);
+ *   - "[BEE-30062] FlashAttention 與高效注意力核心", Background (Flash-Decoding:
+ *     split K/V along the sequence, reduce the partial softmax results
+ *     stably) and section "為長上下文推論啟用 FlashDecoding" (the decode cache
+ *     layout and per-sequence lengths);
+ *   - "Effizienz" (tokenwerk), sections "GQA im leicht lesbaren Code" (query
+ *     head hq reads K/V head hq / (Hq/Hkv)) and "Der wichtige Maskenfehler
+ *     beim Cache" (causal masks carry a position offset when the query is
+ *     shorter than the keys).
+ *
+ * Conventions shared by every entry point.
+ *   - Every tensor pointer is a DEVICE pointer, owned by the caller; all
+ *     tensors are dense and row-major in the layouts stated below. The
+ *     library never allocates, frees or synchronises device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     on it and the call returns without waiting.
+ *   - Scalars and pointers are validated on the host before anything is
+ *     enqueued; on error the call returns a negative attn_status and enqueues
+ *     nothing. Device-resident integers (seq_lens, cache_lens, block tables)
+ *     are not read on the host; the kernels clamp them (stated per call) so
+ *     that no access leaves the buffers the sizes describe.
+ *   - Outputs O have the dtype of Q; LSE is always f32, natural log, in
+ *     scaled-score units: LSE_i = ln Σ_{visible j} exp(scale · q_i·k_j).
+ *     A row that sees no key gets O = 0 and LSE = -inf.
+ *   - Kernels use no atomics: results are bitwise reproducible run to run.
+ *   - The library is stateless and re-entrant.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_EINVAL = -1,       /* bad argument: null pointer, negative size, Hq % Hkv != 0 */
+  ATTN_EUNSUPPORTED = -2, /* valid but not built: dtype, head dim, group size */
+  ATTN_EWORKSPACE = -3,   /* workspace NULL or smaller than attn_decode_workspace_bytes() */
+  ATTN_EHIP = -4          /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Tokens per physical block of a paged cache ("Phase 07 · 12", section
+ * "Paged attention": the cache is cut into 16-token blocks). */
+#define ATTN_BLOCK_TOKENS 16
+
+/*
+ * Prefill over whole prompts.
+ *   q, o : [B, Hq, Nq, d]   (batch, heads, seq, head_dim — the layout of the
+ *                            SDPA call on "[BEE-30062]")
+ *   k, v : [B, Hkv, Nk, d]
+ *   lse  : [B, Hq, Nq] f32, or NULL to skip it
+ * Query head hq uses K/V head hq / (Hq/Hkv). Row i of every head sits at
+ * position i + q_offset; with causal != 0 it sees key j iff j <= i + q_offset
+ * (q_offset = Nk - Nq aligns the last query with the last key; 0 is the usual
+ * square prefill). Without causal every row sees all Nk keys.
+ * Supported: dtype ATTN_BF16 (bf16 inputs, fp32 accumulation, MFMA) and
+ * ATTN_F32 (fp32 throughout), d in {64, 128}. Nq, Nk, B may be 0.
+ * |q_offset| <= 2^30.
+ */
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, int q_offset, void* stream);
+
+/*
+ * Decode of Nq new tokens per sequence against a K/V cache, split along the
+ * key sequence (Flash-Decoding, "[BEE-30062]" Background) and merged with a
+ * log-sum-exp combine.
+ *   q, o        : [B, Nq, Hq, d]  ("[BEE-30062]", "為長上下文推論啟用
+ *                                   FlashDecoding": (batch, 1, n_heads, head_dim))
+ *   lse         : [B, Hq, Nq] f32, or NULL to skip it
+ *   paged cache : block_table != NULL. k_cache, v_cache are pools
+ *                 [num_blocks, 16, Hkv, d]; block_table is
+ *                 [B, max_blocks_per_seq] int32; logical token t of sequence b
+ *                 lives in block block_table[b][t / 16], slot t % 16.
+ *   contiguous  : block_table == NULL. k_cache, v_cache are
+ *                 [B, max_seq_len, Hkv, d] (max_blocks_per_seq, num_blocks
+ *                 are ignored).
+ *   seq_lens    : [B] int32, visible keys of sequence b INCLUDING the Nq new
+ *                 tokens (already appended with kv_append). Query row i of
+ *                 sequence b sits at position seq_lens[b] - Nq + i; with
+ *                 causal it sees keys j <= that position ("Effizienz",
+ *                 "Der wichtige Maskenfehler beim Cache"), without causal all
+ *                 seq_lens[b] keys.
+ *   max_seq_len : an upper bound of seq_lens; it sizes the split grid.
+ *                 Device-side, seq_lens[b] is clamped to [0, max_seq_len]
+ *                 (and to max_blocks_per_seq·16 when paged). Table entries
+ *                 outside [0, num_blocks) make their 16 keys invisible.
+ *   num_splits  : key chunks per (sequence, K/V head); 0 picks a default.
+ *   workspace   : device scratch of at least attn_decode_workspace_bytes()
+ *                 bytes for the same arguments; it holds each chunk's partial
+ *                 output and LSE between the partial and combine kernels.
+ * Supported: dtype ATTN_BF16, d in {64, 128}, (Hq/Hkv)·Nq <= 16.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                      const int32_t* seq_lens, void* o, float* lse,
+                      int dtype, int B, int Hq, int Hkv, int Nq, int d,
+                      float scale, int causal, int max_seq_len, int num_splits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Split count attn_decode_paged uses for these arguments (num_splits = 0:
+ * the default), or a negative attn_status. */
+int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
+                           int num_splits);
+
+/* Workspace bytes attn_decode_paged needs for these arguments; 0 if they are
+ * invalid. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
+                                   int num_splits);
+
+/*
+ * Append Nnew new K/V rows per sequence to the cache (the decode step grows
+ * the cache by concatenation: "大模型面试笔记——Attention篇" §4; "Phase 07 ·
+ * 12", "Build it, step 1").
+ *   k_new, v_new : [B, Nnew, Hkv, d]
+ *   k_cache, v_cache, block_table, max_blocks_per_seq, num_blocks,
+ *   max_seq_len  : as for attn_decode_paged (block_table NULL = contiguous).
+ *   cache_lens   : [B] int32, lengths BEFORE the append. Row r of sequence b
+ *                  goes to logical position cache_lens[b] + r.
+ * The caller owns block allocation: the table must already cover positions
+ * < cache_lens[b] + Nnew; lengths are not updated here (after the call the
+ * caller uses seq_lens = cache_lens + Nnew). A row whose position is negative,
+ * at or beyond max_seq_len, beyond the table, or in a block outside
+ * [0, num_blocks) is not written. The copy is bit-exact.
+ * Supported: dtype ATTN_BF16 or ATTN_F32, d in {64, 128}.
+ */
+int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+              const int32_t* cache_lens, int dtype, int B, int Hkv, int Nnew, int d,
+              int max_seq_len, void* stream);
+
+/*
+ * Gather the first seq_lens[b] logical rows of every sequence out of a paged
+ * (or, with block_table NULL, contiguous) cache into out [B, max_seq_len,
+ * Hkv, d], using the same address computation as attn_decode_paged. Rows at
+ * or beyond the clamped length are left untouched; keys in invalid blocks are
+ * not copied. Exists so tests can check the page-table walk bit for bit.
+ */
+int attn_gather_paged(const void* cache, const int32_t* block_table, int max_blocks_per_seq,
+                      int num_blocks, const int32_t* seq_lens, void* out, int dtype, int B,
+                      int Hkv, int d, int max_seq_len, void* stream);
+
+/* A static string naming a status code. */
+const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

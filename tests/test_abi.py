@@ -1,0 +1,143 @@
+"""The C-ABI library loads, exports every function include/attn.h declares, and
+rejects bad arguments on the host before touching the GPU (CPU only).
+
+No compute call is made here: every call below fails validation, which the
+library performs before its first HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_flashattention_amd as eta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(eta.LIB_PATH),
+                                reason="libattn.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\**([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for n in ("attn_prefill", "attn_decode_paged", "kv_append", "attn_decode_workspace_bytes",
+              "attn_decode_num_splits", "attn_gather_paged", "attn_strerror"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(eta.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), f"{n} declared in attn.h but not exported"
+
+
+def test_strerror():
+    lib = eta.library()
+    assert lib.attn_strerror(0) == b"ok"
+    assert b"invalid" in lib.attn_strerror(-1)
+    assert b"workspace" in lib.attn_strerror(-3)
+    assert lib.attn_strerror(12345) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)  # never dereferenced: every call below fails validation first
+
+
+def _prefill(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, dtype=1, B=1, Hq=4, Hkv=2, Nq=8, Nk=8,
+             d=128, scale=0.1, causal=1, q_offset=0)
+    a.update(kw)
+    return eta.library().attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dtype"], a["B"],
+                                      a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                      a["causal"], a["q_offset"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hq=6, Hkv=4), eta.ATTN_EINVAL),
+    (dict(Hkv=0), eta.ATTN_EINVAL),
+    (dict(B=-1), eta.ATTN_EINVAL),
+    (dict(Nk=-3), eta.ATTN_EINVAL),
+    (dict(scale=0.0), eta.ATTN_EINVAL),
+    (dict(scale=float("nan")), eta.ATTN_EINVAL),
+    (dict(scale=-1.0), eta.ATTN_EINVAL),
+    (dict(q_offset=(1 << 30) + 1), eta.ATTN_EINVAL),
+    (dict(q_offset=-(1 << 30) - 1), eta.ATTN_EINVAL),
+    (dict(d=96), eta.ATTN_EUNSUPPORTED),
+    (dict(dtype=7), eta.ATTN_EUNSUPPORTED),
+    (dict(q=None), eta.ATTN_EINVAL),
+    (dict(k=None), eta.ATTN_EINVAL),
+    (dict(q=P(0x10004)), eta.ATTN_EINVAL),  # not 16-byte aligned
+])
+def test_prefill_rejects(kw, code):
+    assert code != eta.ATTN_OK  # a passing call would launch on fake pointers
+    assert _prefill(**kw) == code
+
+
+def test_prefill_empty_is_ok_without_gpu_work():
+    assert _prefill(B=0) == eta.ATTN_OK
+    assert _prefill(Nq=0) == eta.ATTN_OK
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=None, mb=0, nb=0, sl=FAKE, o=FAKE, lse=None, dtype=1, B=2,
+             Hq=32, Hkv=8, Nq=4, d=128, scale=0.1, causal=1, L=4096, S=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return eta.library().attn_decode_paged(a["q"], a["k"], a["v"], a["bt"], a["mb"], a["nb"],
+                                           a["sl"], a["o"], a["lse"], a["dtype"], a["B"], a["Hq"],
+                                           a["Hkv"], a["Nq"], a["d"], a["scale"], a["causal"],
+                                           a["L"], a["S"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), eta.ATTN_EUNSUPPORTED),       # fp32 decode not built
+    (dict(Nq=5), eta.ATTN_EUNSUPPORTED),          # 4 heads x 5 rows > 16
+    (dict(d=80), eta.ATTN_EUNSUPPORTED),
+    (dict(Hq=30), eta.ATTN_EINVAL),
+    (dict(L=-1), eta.ATTN_EINVAL),
+    (dict(S=-2), eta.ATTN_EINVAL),
+    (dict(sl=None), eta.ATTN_EINVAL),
+    (dict(bt=FAKE, mb=0), eta.ATTN_EINVAL),
+    (dict(ws=None), eta.ATTN_EWORKSPACE),
+    (dict(wsb=16), eta.ATTN_EWORKSPACE),
+    (dict(scale=float("inf")), eta.ATTN_EINVAL),
+])
+def test_decode_rejects(kw, code):
+    assert code != eta.ATTN_OK
+    assert _decode(**kw) == code
+
+
+def test_split_plan_and_workspace_size():
+    lib = eta.library()
+    # 16 sequences x 8 K/V heads x 32768 keys: 512-key chunks, 64 splits
+    assert lib.attn_decode_num_splits(16, 32, 8, 1, 128, 32768, 0) == 64
+    assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 100, 0) == 1
+    assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 1000, 3) == 3
+    assert lib.attn_decode_num_splits(1, 32, 8, 5, 128, 1000, 0) == eta.ATTN_EUNSUPPORTED
+    # rows = B*Hkv*splits*G*Nq; O partials f32 (256-byte padded) then f32 LSE per row
+    rows = 16 * 8 * 64 * 4
+    assert lib.attn_decode_workspace_bytes(16, 32, 8, 1, 128, 32768, 0) == rows * 128 * 4 + rows * 4
+    assert lib.attn_decode_workspace_bytes(16, 32, 8, 9, 128, 32768, 0) == 0
+
+
+def test_kv_append_and_gather_reject():
+    lib = eta.library()
+    # Hkv = 0
+    assert lib.kv_append(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 1, 1, 0, 1, 128, 16, None) == -1
+    # unsupported d
+    assert lib.kv_append(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 1, 1, 2, 1, 48, 16, None) == -2
+    # missing cache_lens
+    assert lib.kv_append(FAKE, FAKE, FAKE, FAKE, None, 0, 0, None, 1, 1, 2, 1, 128, 16, None) == -1
+    # paged without a table width
+    assert lib.attn_gather_paged(FAKE, FAKE, 0, 4, FAKE, FAKE, 1, 1, 2, 128, 16, None) == -1
+    # nothing to do
+    assert lib.kv_append(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 1, 0, 2, 1, 128, 16, None) == 0
