@@ -54,9 +54,46 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--long-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only-prefill", action="store_true",
-                    help="time only the 4k prefill stage (for profiling runs)")
+    ap.add_argument("--stage", default=None,
+                    choices=["prefill_4k", "prefill_32k", "splitkv_decode_32k", "paged_decode_q4",
+                             "copy_1gib"],
+                    help="run only this stage --steps times and exit (for profiler runs); "
+                         "copy_1gib is a plain 1 GiB device copy used to calibrate HBM counters")
     return ap.parse_args()
+
+
+def run_stage(args, torch, eta, inputs, dev):
+    """One stage alone, --warmup + --steps launches, one summary line on stderr."""
+    name = args.stage
+    if name == "copy_1gib":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)  # noqa: E731
+    elif name in ("prefill_4k", "prefill_32k"):
+        wl = "causal_gqa_prefill_4k" if name == "prefill_4k" else "causal_gqa_prefill_32k"
+        q, k, v = inputs.workload_inputs(wl, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fn = lambda: eta.attn_prefill(q, k, v, causal=True, out=o, lse=lse)  # noqa: E731
+    elif name == "splitkv_decode_32k":
+        q, kc, vc, sl = inputs.workload_inputs(name, dev)
+        fn = lambda: eta.attn_decode_paged(q, kc, vc, sl, causal=True)  # noqa: E731
+    else:
+        p = inputs.workload_inputs(name, dev)
+        eta.kv_append(p["k_new"], p["v_new"], p["k_pool"], p["v_pool"], p["cache_lens"],
+                      block_table=p["block_table"])
+        fn = lambda: eta.attn_decode_paged(p["q"], p["k_pool"], p["v_pool"], p["seq_lens"],  # noqa
+                                           block_table=p["block_table"], causal=True)
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(f"[bench] stage {name}: {args.steps} launches, {dt * 1e3:.4f} ms each (wall)",
+          file=sys.stderr, flush=True)
 
 
 class StageTimer:
@@ -129,6 +166,9 @@ def main():
         sys.exit(2)
     eta.library()
     dev = torch.device("cuda:0")
+    if args.stage is not None:
+        run_stage(args, torch, eta, inputs, dev)
+        return
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] device {torch.cuda.get_device_name(dev)}; building inputs", file=sys.stderr,
           flush=True)
@@ -168,10 +208,8 @@ def main():
     def decode4():
         eta.attn_decode_paged(q4, kc4, vc4, sl4, causal=True, workspace=ws4, out=o4, lse=l4)
 
-    stages = [("prefill_4k", prefill4k)]
-    if not args.only_prefill:
-        stages += [("kv_append_q4", append5), ("paged_decode_q4", decode5),
-                   ("splitkv_decode_32k", decode4)]
+    stages = [("prefill_4k", prefill4k), ("kv_append_q4", append5),
+              ("paged_decode_q4", decode5), ("splitkv_decode_32k", decode4)]
     timer = StageTimer(torch, stream, [n for n, _ in stages])
 
     for _ in range(args.warmup):
@@ -194,47 +232,46 @@ def main():
                                   "frac_of_peak": round(tflops2 / PEAK_BF16_TFLOPS, 4),
                                   "flops": flops2},
     }
-    if not args.only_prefill:
-        bytes4 = 2 * 2 * w4["Hkv"] * w4["d"] * w4["B"] * w4["seq_len"]
-        ms4 = timer.mean_ms("splitkv_decode_32k")
-        bytes5 = 2 * 2 * w5["Hkv"] * w5["d"] * sum(seq5)
-        ms5 = timer.mean_ms("paged_decode_q4")
-        msa = timer.mean_ms("kv_append_q4")
-        result_workloads["splitkv_decode_32k"] = {
-            "ms": round(ms4, 5), "GB/s": round(bytes4 / (ms4 * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(bytes4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "kv_bytes": bytes4}
-        result_workloads["paged_decode_q4"] = {
-            "ms": round(ms5, 5), "GB/s": round(bytes5 / (ms5 * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(bytes5 / (ms5 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "kv_bytes": bytes5, "kv_append_ms": round(msa, 5)}
+    bytes4 = 2 * 2 * w4["Hkv"] * w4["d"] * w4["B"] * w4["seq_len"]
+    ms4 = timer.mean_ms("splitkv_decode_32k")
+    bytes5 = 2 * 2 * w5["Hkv"] * w5["d"] * sum(seq5)
+    ms5 = timer.mean_ms("paged_decode_q4")
+    msa = timer.mean_ms("kv_append_q4")
+    result_workloads["splitkv_decode_32k"] = {
+        "ms": round(ms4, 5), "GB/s": round(bytes4 / (ms4 * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(bytes4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "kv_bytes": bytes4}
+    result_workloads["paged_decode_q4"] = {
+        "ms": round(ms5, 5), "GB/s": round(bytes5 / (ms5 * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(bytes5 / (ms5 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "kv_bytes": bytes5, "kv_append_ms": round(msa, 5)}
 
-        # long-context prefill and the fp32 single-head case, in their own loops
-        print("[bench] long-context prefill", file=sys.stderr, flush=True)
-        del kc4, vc4
-        torch.cuda.empty_cache()
-        q3, k3, v3 = inputs.workload_inputs("causal_gqa_prefill_32k", dev)
-        o3 = torch.empty_like(q3)
-        l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
-        t3 = StageTimer(torch, stream, ["p"])
-        eta.attn_prefill(q3, k3, v3, causal=True, out=o3, lse=l3)
-        for _ in range(max(1, args.long_steps)):
-            t3.run("p", lambda: eta.attn_prefill(q3, k3, v3, causal=True, out=o3, lse=l3))
-        torch.cuda.synchronize()
-        ms3 = t3.mean_ms("p")
-        flops3 = prefill_flops(1, 32, 32768, 128)
-        result_workloads["causal_gqa_prefill_32k"] = {
-            "ms": round(ms3, 4), "TFLOP/s": round(flops3 / (ms3 * 1e-3) / 1e12, 2),
-            "frac_of_peak": round(flops3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "flops": flops3}
-        q1, k1, v1 = inputs.workload_inputs("single_head_f32", dev)
-        t1 = StageTimer(torch, stream, ["p"])
-        for _ in range(10):
-            eta.attn_prefill(q1, k1, v1, causal=False)
-        for _ in range(50):
-            t1.run("p", lambda: eta.attn_prefill(q1, k1, v1, causal=False))
-        torch.cuda.synchronize()
-        result_workloads["single_head_f32"] = {"us": round(t1.mean_ms("p") * 1e3, 2)}
+    # long-context prefill and the fp32 single-head case, in their own loops
+    print("[bench] long-context prefill", file=sys.stderr, flush=True)
+    del kc4, vc4
+    torch.cuda.empty_cache()
+    q3, k3, v3 = inputs.workload_inputs("causal_gqa_prefill_32k", dev)
+    o3 = torch.empty_like(q3)
+    l3 = torch.empty(q3.shape[:3], dtype=torch.float32, device=dev)
+    t3 = StageTimer(torch, stream, ["p"])
+    eta.attn_prefill(q3, k3, v3, causal=True, out=o3, lse=l3)
+    for _ in range(max(1, args.long_steps)):
+        t3.run("p", lambda: eta.attn_prefill(q3, k3, v3, causal=True, out=o3, lse=l3))
+    torch.cuda.synchronize()
+    ms3 = t3.mean_ms("p")
+    flops3 = prefill_flops(1, 32, 32768, 128)
+    result_workloads["causal_gqa_prefill_32k"] = {
+        "ms": round(ms3, 4), "TFLOP/s": round(flops3 / (ms3 * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(flops3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flops": flops3}
+    q1, k1, v1 = inputs.workload_inputs("single_head_f32", dev)
+    t1 = StageTimer(torch, stream, ["p"])
+    for _ in range(10):
+        eta.attn_prefill(q1, k1, v1, causal=False)
+    for _ in range(50):
+        t1.run("p", lambda: eta.attn_prefill(q1, k1, v1, causal=False))
+    torch.cuda.synchronize()
+    result_workloads["single_head_f32"] = {"us": round(t1.mean_ms("p") * 1e3, 2)}
 
     roofline = {"bound": "mfma", "achieved": round(tflops2, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops2 / PEAK_BF16_TFLOPS, 4),

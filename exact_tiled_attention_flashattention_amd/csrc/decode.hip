@@ -60,11 +60,19 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {
   return __builtin_amdgcn_perm(y, x, 0x07060302u);
 }
 
+// K/V of one 32-key step, in the registers the MFMAs consume.
+template <int D>
+struct StepRegs {
+  bf16x8_t kf[2][D / 32];  // A operand of Sᵀ: lane = key (r16) of half h2, 8 d at 32c + 8g
+  u32x4_t vv[2][4];        // 8 d (chunk r16) of keys 16*h2 + 4*g + jj
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   constexpr int NC = D / 32;  // MFMAs per 16 keys for Sᵀ (32 d each)
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform indices live in scalar registers
+  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (wid >= p.B * p.Hkv * p.S) return;
   const int split = wid % p.S;
   const int bk = wid / p.S;
@@ -76,6 +84,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
   const int kb0 = split * p.chunk;
   const int ke = min(n, kb0 + p.chunk);
+  if (kb0 >= ke) return;  // empty chunk: the combine never reads it
   float* po = p.part_o + ((long long)bk * p.S + split) * p.M * D;
   float* pl = p.part_lse + ((long long)bk * p.S + split) * p.M;
 
@@ -107,40 +116,35 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   const __bf16* vbase = p.v + (long long)kvh * D;
   const bool v_lane = (8 * r16) < D;  // lanes whose 8-wide d chunk exists
 
-  for (int k0 = kb0; k0 < ke; k0 += 32) {
-    long long row0[2];
-    row0[0] = cache_row(p.cv, b, k0);
-    row0[1] = cache_row(p.cv, b, k0 + 16);
-
-    // ---- loads: K into the A operand, V as 8 consecutive d of 8 keys -------
-    bf16x8_t kf[2][NC];
-    u32x4_t vv[2][4];
+  // Every 16-key half of a step is one cache block (chunks start at multiples
+  // of 32); row0 is the element offset of its first token, -1 if invalid.
+  auto load = [&](int k0, const long long row0[2], StepRegs<D>& r) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const int key = k0 + 16 * h2 + r16;
-      const bool ok = row0[h2] >= 0 && key < ke;
+      const bool ok = row0[h2] >= 0 && (k0 + 16 * h2 + r16) < ke;
       const __bf16* kp = kbase + row0[h2] + (long long)r16 * rstride + 8 * g;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        kf[h2][c] = ok ? *reinterpret_cast<const bf16x8_t*>(kp + 32 * c) : bf16x8_t{};
+        r.kf[h2][c] = ok ? *reinterpret_cast<const bf16x8_t*>(kp + 32 * c) : bf16x8_t{};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int vk = 4 * g + jj;
         const bool vok = v_lane && row0[h2] >= 0 && (k0 + 16 * h2 + vk) < ke;
-        vv[h2][jj] = vok ? *reinterpret_cast<const u32x4_t*>(vbase + row0[h2] +
-                                                             (long long)vk * rstride + 8 * r16)
-                         : u32x4_t{0, 0, 0, 0};
+        r.vv[h2][jj] = vok ? *reinterpret_cast<const u32x4_t*>(vbase + row0[h2] +
+                                                               (long long)vk * rstride + 8 * r16)
+                           : u32x4_t{0, 0, 0, 0};
       }
     }
+  };
 
-    // ---- Sᵀ[key][row] ---------------------------------------------------------
+  auto compute = [&](int k0, const long long row0[2], const StepRegs<D>& r) {
     f32x4_t s[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       s[h2] = f32x4_t{};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[h2][c], qf[c], s[h2], 0, 0, 0);
+        s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.kf[h2][c], qf[c], s[h2], 0, 0, 0);
     }
     float mx = neg_inf();
 #pragma unroll
@@ -171,26 +175,51 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] *= alpha;
 
-    // ---- Oᵀ += Vᵀ Pᵀ: key slot j of lane group g is key 16*(j/4) + 4*g + j%4 ----
+    // Oᵀ += Vᵀ Pᵀ: key slot j of lane group g is key 16*(j/4) + 4*g + j%4
     const bf16x4_t p0 = __builtin_convertvector(s[0], bf16x4_t);
     const bf16x4_t p1 = __builtin_convertvector(s[1], bf16x4_t);
     const bf16x8_t pb = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {  // dword e of each V chunk holds d = 8*r16 + 2e, 2e+1
       u32x4_t lo, hi;
-      lo[0] = perm_lo(vv[0][0][e], vv[0][1][e]);
-      lo[1] = perm_lo(vv[0][2][e], vv[0][3][e]);
-      lo[2] = perm_lo(vv[1][0][e], vv[1][1][e]);
-      lo[3] = perm_lo(vv[1][2][e], vv[1][3][e]);
-      hi[0] = perm_hi(vv[0][0][e], vv[0][1][e]);
-      hi[1] = perm_hi(vv[0][2][e], vv[0][3][e]);
-      hi[2] = perm_hi(vv[1][0][e], vv[1][1][e]);
-      hi[3] = perm_hi(vv[1][2][e], vv[1][3][e]);
+      lo[0] = perm_lo(r.vv[0][0][e], r.vv[0][1][e]);
+      lo[1] = perm_lo(r.vv[0][2][e], r.vv[0][3][e]);
+      lo[2] = perm_lo(r.vv[1][0][e], r.vv[1][1][e]);
+      lo[3] = perm_lo(r.vv[1][2][e], r.vv[1][3][e]);
+      hi[0] = perm_hi(r.vv[0][0][e], r.vv[0][1][e]);
+      hi[1] = perm_hi(r.vv[0][2][e], r.vv[0][3][e]);
+      hi[2] = perm_hi(r.vv[1][0][e], r.vv[1][1][e]);
+      hi[3] = perm_hi(r.vv[1][2][e], r.vv[1][3][e]);
       acc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), pb,
                                                            acc[2 * e], 0, 0, 0);
       acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
                                                                pb, acc[2 * e + 1], 0, 0, 0);
     }
+  };
+
+  // software pipeline: the next step's block lookups and loads are issued
+  // before the current step is computed
+  StepRegs<D> ra, rb;
+  long long rowa[2], rowb[2];
+  rowa[0] = cache_row(p.cv, b, kb0);
+  rowa[1] = cache_row(p.cv, b, kb0 + 16);
+  load(kb0, rowa, ra);
+  for (int k0 = kb0; k0 < ke; k0 += 64) {
+    const bool more1 = k0 + 32 < ke;
+    if (more1) {
+      rowb[0] = cache_row(p.cv, b, k0 + 32);
+      rowb[1] = cache_row(p.cv, b, k0 + 48);
+      load(k0 + 32, rowb, rb);
+    }
+    compute(k0, rowa, ra);
+    if (!more1) break;
+    const bool more2 = k0 + 64 < ke;
+    if (more2) {
+      rowa[0] = cache_row(p.cv, b, k0 + 64);
+      rowa[1] = cache_row(p.cv, b, k0 + 80);
+      load(k0 + 64, rowa, ra);
+    }
+    compute(k0 + 32, rowb, rb);
   }
 
   // ---- partial result of this chunk --------------------------------------------
@@ -213,10 +242,17 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   }
 }
 
-// One workgroup of D threads per (sequence, K/V head, query row).
+// One workgroup of 4 waves per (sequence, K/V head, query row). Wave w merges
+// the chunks s = w, w+4, ... with weights exp2(LSE_s - max); the four partial
+// sums are added in a fixed order through LDS, so the result is deterministic.
+// Each lane owns D/64 consecutive output elements.
 template <int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+  constexpr int E = D / 64;  // elements per lane
+  __shared__ float red_acc[4][D];
+  __shared__ float red_tot[4];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int r = blockIdx.x % p.M;
   const int bk = blockIdx.x / p.M;
   const int b = bk / p.Hkv;
@@ -226,24 +262,60 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeParams p) {
   const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
   const int used = min(p.S, (n + p.chunk - 1) / p.chunk);
   const float* pl = p.part_lse + (long long)bk * p.S * p.M + r;
-  const float* po = p.part_o + ((long long)bk * p.S * p.M + r) * D + d;
+  const float* po = p.part_o + ((long long)bk * p.S * p.M + r) * D + E * lane;
 
   float mx = neg_inf();
   for (int s = 0; s < used; ++s) mx = fmaxf(mx, pl[(long long)s * p.M]);
-  float tot = 0.f, acc = 0.f;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float tot = 0.f;
   if (mx != neg_inf()) {
-    for (int s = 0; s < used; ++s) {
+    int s = wave;
+    for (; s + 12 < used; s += 16) {  // four chunks in flight per lane
+      float w[4];
+      float v[4][E];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float ls = pl[(long long)(s + 4 * u) * p.M];
+        w[u] = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[u][e] = po[(long long)(s + 4 * u) * p.M * D + e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tot += w[u];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(w[u], v[u][e], acc[e]);
+      }
+    }
+    for (; s < used; s += 4) {
       const float ls = pl[(long long)s * p.M];
       const float w = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
       tot += w;
-      acc = __builtin_fmaf(w, po[(long long)s * p.M * D], acc);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        acc[e] = __builtin_fmaf(w, po[(long long)s * p.M * D + e], acc[e]);
     }
   }
-  const float out = tot > 0.f ? acc / tot : 0.f;
-  p.o[(((long long)b * p.Nq + qi) * p.Hq + hq) * D + d] = (__bf16)out;
-  if (d == 0 && p.lse != nullptr)
-    p.lse[((long long)b * p.Hq + hq) * p.Nq + qi] =
-        tot > 0.f ? (mx + __builtin_amdgcn_logf(tot)) * kLn2 : neg_inf();
+#pragma unroll
+  for (int e = 0; e < E; ++e) red_acc[wave][E * lane + e] = acc[e];
+  if (lane == 0) red_tot[wave] = tot;
+  __syncthreads();
+  if (wave == 0) {
+    const float t = (red_tot[0] + red_tot[1]) + (red_tot[2] + red_tot[3]);
+    const float inv = t > 0.f ? 1.f / t : 0.f;
+    __bf16* op = p.o + (((long long)b * p.Nq + qi) * p.Hq + hq) * D + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = E * lane + e;
+      const float a = (red_acc[0][d] + red_acc[1][d]) + (red_acc[2][d] + red_acc[3][d]);
+      op[e] = (__bf16)(a * inv);
+    }
+    if (lane == 0 && p.lse != nullptr)
+      p.lse[((long long)b * p.Hq + hq) * p.Nq + qi] =
+          t > 0.f ? (mx + __builtin_amdgcn_logf(t)) * kLn2 : neg_inf();
+  }
 }
 
 }  // namespace
@@ -283,12 +355,12 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((int)blocks), dim3(256), 0, s, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int)cblocks), dim3(128), 0, s, pp);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int)cblocks), dim3(256), 0, s, pp);
   } else {
     hipLaunchKernelGGL(decode_partial_kernel<64>, dim3((int)blocks), dim3(256), 0, s, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int)cblocks), dim3(64), 0, s, pp);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int)cblocks), dim3(256), 0, s, pp);
   }
   return hipGetLastError();
 }

@@ -35,7 +35,8 @@ namespace attn {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = 64;         // keys per tile
+constexpr float kTau = 8.0f;    // rescale only when a row max grows by more than 2^8
 
 struct PrefillParams {
   const __bf16* q;
@@ -53,26 +54,38 @@ struct PrefillParams {
   int q_offset;
 };
 
+// K/V tiles live in LDS unpadded (D*2 bytes per key row) with the 16-byte
+// chunks of row r permuted by chunk ^ swz(r). The permutation makes both LDS
+// read patterns conflict-free: the K reads (16 consecutive rows, one chunk)
+// and the transposing V reads (4 consecutive rows x 4 chunks per 32 lanes).
 template <int D>
-struct Smem {
-  static constexpr int kStride = D + 8;  // bf16 per LDS row: 16-byte pad against bank conflicts
-  static constexpr int kTile = kBN * kStride;
-  static constexpr int kChunks = kBN * D / 8;       // 16-byte chunks per K (or V) tile
-  static constexpr int kPerThread = kChunks / (kWaves * 64);
-};
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return (row >> 1) & 7;
+}
+
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int elem) {  // byte offset of element (row, elem)
+  return row * (D * 2) + ((((elem >> 3) ^ swz<D>(row))) << 4) + ((elem & 7) << 1);
+}
 
 template <int D, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillParams p) {
-  constexpr int NDC = D / 16;  // k-steps of the Q·Kᵀ contraction
-  constexpr int NDB = D / 32;  // 32-row blocks of Oᵀ
-  constexpr int STR = Smem<D>::kStride;
-  constexpr int TILE = Smem<D>::kTile;
-  constexpr int NL = Smem<D>::kPerThread;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * 2 * TILE];  // [stage][K, V][tile]
+  constexpr int NDC = D / 16;              // k-steps of the Q·Kᵀ contraction
+  constexpr int NDB = D / 32;              // 32-row blocks of Oᵀ
+  constexpr int CPR = D / 8;               // 16-byte chunks per key row
+  constexpr int TILE = kBN * D * 2;        // bytes of one K (or V) tile
+  constexpr int NI = TILE / (kWaves * 1024);  // direct loads per wave per tile and tensor
+  // two stages as two LDS objects, so that reads of one stage and the
+  // in-flight direct loads into the other are provably disjoint
+  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // [K, V]
+  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -100,8 +113,7 @@ void prefill_bf16_kernel(PrefillParams p) {
     if (lim < kend) kend = (int)(lim < 0 ? 0 : lim);
   }
   const int ntiles = (kend + kBN - 1) / kBN;
-  // first key index at which some row of the workgroup needs masking
-  long long mask_from = p.Nk;
+  long long mask_from = p.Nk;  // first key some row of the workgroup cannot see
   if (CAUSAL) {
     const long long first = (long long)q0 + p.q_offset + 1;
     if (first < mask_from) mask_from = first;
@@ -124,61 +136,49 @@ void prefill_bf16_kernel(PrefillParams p) {
   const __bf16* kg = p.k + kv_base;
   const __bf16* vg = p.v + kv_base;
 
-  u32x4_t kr[NL], vr[NL];
-  auto gload = [&](int k0) {
+  // Direct global->LDS loads: instruction i of this wave fills LDS bytes
+  // [(wave*NI + i)*1024, +1024) of the tile, lane l its 16 bytes at +16*l, i.e.
+  // physical chunk (lin % CPR) of row (lin / CPR). The lane fetches the logical
+  // chunk that the swizzle stores there. Rows past Nk re-read row Nk-1 (finite
+  // values; those keys are masked).
+  auto issue = [&](int k0, char* buf) {
+    char* kd = buf;
+    char* vd = buf + TILE;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = tid + i * kWaves * 64;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      if (k0 + row < p.Nk) {
-        const long long off = (long long)(k0 + row) * D + col;
-        kr[i] = *reinterpret_cast<const u32x4_t*>(kg + off);
-        vr[i] = *reinterpret_cast<const u32x4_t*>(vg + off);
-      } else {
-        kr[i] = u32x4_t{0, 0, 0, 0};
-        vr[i] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    __bf16* kl = lds + stage * 2 * TILE;
-    __bf16* vl = kl + TILE;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = tid + i * kWaves * 64;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4_t*>(kl + row * STR + col) = kr[i];
-      *reinterpret_cast<u32x4_t*>(vl + row * STR + col) = vr[i];
+    for (int i = 0; i < NI; ++i) {
+      const int lin = (wave * NI + i) * 64 + lane;
+      const int row = lin / CPR;
+      const int chunk = (lin % CPR) ^ swz<D>(row);
+      const int grow = min(k0 + row, p.Nk - 1);
+      const long long off = (long long)grow * D + chunk * 8;
+      __builtin_amdgcn_global_load_lds(kg + off, (ATTN_LDS void*)(kd + (wave * NI + i) * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vg + off, (ATTN_LDS void*)(vd + (wave * NI + i) * 1024),
+                                       16, 0, 0);
     }
   };
 
   f32x16_t acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
-  float m_run = neg_inf();
-  float l_run = 0.f;
+  float m_run = neg_inf();  // reference max (base 2) of this lane's row
+  float l_run = 0.f;        // this lane's share of the row sum of P
 
   // transposing-read address pattern inside a 16-lane group
-  const int grp = lane >> 4;     // 0..3
-  const int src = lane & 15;     // lane index inside the group
-  const int tr_row = src >> 2;   // row offset 0..3
+  const int grp = lane >> 4;
+  const int src = lane & 15;
+  const int tr_row = src >> 2;
   const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
 
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int stage = it & 1;
+  // one tile: wait for it in `cur`, start the next one into `nxt`, compute
+  auto step = [&](int it, const char* cur, char* nxt) {
     const int k0 = it * kBN;
-    if (it + 1 < ntiles) gload(k0 + kBN);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile `it` landed
+    __syncthreads();                     // ... and every other wave's; `nxt` is free again
+    if (it + 1 < ntiles) issue(k0 + kBN, nxt);
 
-    const __bf16* kl = lds + stage * 2 * TILE;
-    const __bf16* vl = kl + TILE;
+    const char* kl = cur;
+    const char* vl = cur + TILE;
 
     // Sᵀ[key][row] for the two 32-key halves of the tile
     f32x16_t s[2];
@@ -187,8 +187,8 @@ void prefill_bf16_kernel(PrefillParams p) {
       s[kb] = f32x16_t{};
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(kl + (kb * 32 + l32) * STR + 16 * dc + 8 * g);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            kl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
       }
     }
@@ -206,63 +206,78 @@ void prefill_bf16_kernel(PrefillParams p) {
         }
     }
 
-    // online softmax (base 2): running max m_run, partial row sum l_run
-    float mx = s[0][0];
+    // tile max of the row (raw scores), tree-reduced, then across the two halves
+    float mq[8];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    for (int j = 0; j < 8; ++j)
+      mq[j] = fmaxf(fmaxf(s[j >> 2][4 * (j & 3)], s[j >> 2][4 * (j & 3) + 1]),
+                    fmaxf(s[j >> 2][4 * (j & 3) + 2], s[j >> 2][4 * (j & 3) + 3]));
+    float mx = fmaxf(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])),
+                     fmaxf(fmaxf(mq[4], mq[5]), fmaxf(mq[6], mq[7])));
     mx = max_across_halves(mx);
-    const float m_new = fmaxf(m_run, mx * p.c);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    const float mt = mx * p.c;
 
-    float rs = 0.f;
+    // online softmax with a lazily moved reference: exp2(s*c - m) stays below
+    // 2^kTau, so the reference only moves (and O, l are rescaled) when the
+    // row max jumps by more than kTau. The result is the same softmax.
+    const bool need = mt > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 from -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+    const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+
+    // P = exp2(s*c - m) in fp32 for the row sum (the LSE needs the unrounded
+    // values), P̃ = bf16(P) packed two per dword in Sᵀ register order for PV
+    uint32_t pk[2][8];
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], p.c, -m_use));
-        s[kb][i] = e;
-        rs += e;
+      for (int j = 0; j < 8; ++j) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j], p.c, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j + 1], p.c, -m_use));
+        ls[(2 * j) & 3] += e0;
+        ls[(2 * j + 1) & 3] += e1;
+        pk[kb][j] = pack_bf16x2(e0, e1);
       }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-    // Oᵀ += Vᵀ Pᵀ, 16 keys per MFMA
+    // Oᵀ += Vᵀ Pᵀ, 16 keys per MFMA; Vᵀ via transposing LDS reads
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        bf16x8_t pb;
-        {
-          f32x4_t lo = {s[kb][8 * hf + 0], s[kb][8 * hf + 1], s[kb][8 * hf + 2], s[kb][8 * hf + 3]};
-          f32x4_t hi = {s[kb][8 * hf + 4], s[kb][8 * hf + 5], s[kb][8 * hf + 6], s[kb][8 * hf + 7]};
-          bf16x4_t l4 = __builtin_convertvector(lo, bf16x4_t);
-          bf16x4_t h4 = __builtin_convertvector(hi, bf16x4_t);
-          pb = bf16x8_t{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-        }
+        const u32x4_t pw4 = {pk[kb][4 * hf], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2],
+                             pk[kb][4 * hf + 3]};
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw4);
+        const int r0 = kb * 32 + 16 * hf + 4 * g + tr_row;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const int col = 32 * db + tr_col;
-          const int r0 = kb * 32 + 16 * hf + 4 * g + tr_row;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (ATTN_LDS i16x4_t*)(vl + r0 * STR + col));
+              (ATTN_LDS i16x4_t*)(vl + lds_off<D>(r0, col)));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (ATTN_LDS i16x4_t*)(vl + (r0 + 8) * STR + col));
-          const bf16x4_t lob = __builtin_bit_cast(bf16x4_t, lo);
-          const bf16x4_t hib = __builtin_bit_cast(bf16x4_t, hi);
-          const bf16x8_t a = {lob[0], lob[1], lob[2], lob[3], hib[0], hib[1], hib[2], hib[3]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[db], 0, 0, 0);
+              (ATTN_LDS i16x4_t*)(vl + lds_off<D>(r0 + 8, col)));
+          const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+          const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a4), pb,
+                                                            acc[db], 0, 0, 0);
         }
       }
+  };
 
-    if (it + 1 < ntiles) lstore(stage ^ 1);
-    __syncthreads();
+  if (ntiles > 0) issue(0, lds0);
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, lds0, lds1);
+    if (it + 1 < ntiles) step(it + 1, lds1, lds0);
   }
 
   // ---- epilogue: O = Oᵀ/l written once, LSE = ln(sum) + max --------------------
