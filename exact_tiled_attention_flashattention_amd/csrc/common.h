@@ -46,10 +46,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// max over the two 32-lane halves of the wave (lanes l and l^32).
+// max over the two 32-lane halves of the wave (lanes l and l^32); NaN-propagating.
 __device__ __forceinline__ float max_across_halves(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float sum_across_halves(float x) {
   auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -58,7 +58,7 @@ __device__ __forceinline__ float sum_across_halves(float x) {
 // the same over lanes l and l^16.
 __device__ __forceinline__ float max_across_rows16(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float sum_across_rows16(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -154,11 +154,11 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
         const int key = k0 + 16 * h2 + 4 * g + i;
         const bool vis = row0[h2] >= 0 && key < limit;
         if (!vis) s[h2][i] = neg_inf();
-        mx = fmaxf(mx, s[h2][i]);
+        mx = __builtin_elementwise_maximum(mx, s[h2][i]);
       }
     mx = max_across_rows16(mx);
     mx = max_across_halves(mx);
-    const float m_new = fmaxf(m_run, mx * p.c);
+    const float m_new = __builtin_elementwise_maximum(m_run, mx * p.c);
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;

@@ -37,6 +37,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBN = 64;         // keys per tile
 constexpr float kTau = 8.0f;    // rescale only when a row max grows by more than 2^8
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, 32-bit dword data
 
 struct PrefillParams {
   const __bf16* q;
@@ -79,10 +80,13 @@ void prefill_bf16_kernel(PrefillParams p) {
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
   constexpr int TILE = kBN * D * 2;        // bytes of one K (or V) tile
   constexpr int NI = TILE / (kWaves * 1024);  // direct loads per wave per tile and tensor
-  // two stages as two LDS objects, so that reads of one stage and the
-  // in-flight direct loads into the other are provably disjoint
-  __shared__ __attribute__((aligned(1024))) char lds0[2 * TILE];  // [K, V]
-  __shared__ __attribute__((aligned(1024))) char lds1[2 * TILE];
+  // K runs one tile ahead of V: tile t's K sits in kb[t % 2], its V in vb[t % 2].
+  // Four separate LDS objects, so the compiler can tell that the in-flight
+  // direct loads never alias the buffers being read.
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,6 +122,11 @@ void prefill_bf16_kernel(PrefillParams p) {
     const long long first = (long long)q0 + p.q_offset + 1;
     if (first < mask_from) mask_from = first;
   }
+  // this lane's last visible key (clamped into int range)
+  long long lim64 = CAUSAL ? (long long)my_q + p.q_offset : (long long)p.Nk - 1;
+  if (lim64 > (long long)p.Nk - 1) lim64 = (long long)p.Nk - 1;
+  if (lim64 < -1) lim64 = -1;
+  const int lim = (int)lim64;
 
   // ---- Qᵀ as the B operand: lane holds row my_q, d = 16*dc + 8*g + j ---------
   bf16x8_t qf[NDC];
@@ -136,25 +145,60 @@ void prefill_bf16_kernel(PrefillParams p) {
   const __bf16* kg = p.k + kv_base;
   const __bf16* vg = p.v + kv_base;
 
-  // Direct global->LDS loads: instruction i of this wave fills LDS bytes
-  // [(wave*NI + i)*1024, +1024) of the tile, lane l its 16 bytes at +16*l, i.e.
-  // physical chunk (lin % CPR) of row (lin / CPR). The lane fetches the logical
-  // chunk that the swizzle stores there. Rows past Nk re-read row Nk-1 (finite
-  // values; those keys are masked).
-  auto issue = [&](int k0, char* buf) {
-    char* kd = buf;
-    char* vd = buf + TILE;
+  // Direct global->LDS loads through buffer resources (one per K/V head, range
+  // Nk rows): instruction i of this wave fills LDS bytes
+  // [(wave*NI + i)*1024, +1024), lane l its 16 bytes at +16*l, i.e. physical
+  // chunk (lin % CPR) of row (lin / CPR); the lane fetches the logical chunk
+  // that the swizzle stores there. The per-lane byte offsets do not depend on
+  // the tile; rows at or past Nk fall outside the resource and arrive as zeros
+  // (those keys are masked).
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, p.Nk * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, p.Nk * D * 2, kBufferFlags);
+  // Lane part of the byte offset: instruction i of the wave adds
+  // (wave*NI + i)*1024 (scalar) and flips the chunk bits that the swizzle
+  // takes from the row's instruction index (one XOR). For d = 128 a
+  // 1 KiB instruction covers rows 4*(wave*NI+i) + lane/16, swz = 4*(lane/16) + i;
+  // for d = 64 rows 8*(wave*NI+i) + lane/8, swz = 4*i + lane/16.
+  const int lane_base = (D == 128)
+      ? ((lane >> 4) * 256) | (16 * ((lane & 15) ^ (4 * (lane >> 4))))
+      : ((lane >> 3) * 128) | (16 * ((lane & 7) ^ (lane >> 4)));
+  constexpr int kXorStep = (D == 128) ? 16 : 64;
+  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int k0, char* dst) {
+    int lb = lane_base;
+    asm volatile("" : "+v"(lb));  // recompute the offsets here instead of keeping them live
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int lin = (wave * NI + i) * 64 + lane;
-      const int row = lin / CPR;
-      const int chunk = (lin % CPR) ^ swz<D>(row);
-      const int grow = min(k0 + row, p.Nk - 1);
-      const long long off = (long long)grow * D + chunk * 8;
-      __builtin_amdgcn_global_load_lds(kg + off, (ATTN_LDS void*)(kd + (wave * NI + i) * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + off, (ATTN_LDS void*)(vd + (wave * NI + i) * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(dst + (wave * NI + i) * 1024),
+                                               16, lb ^ (kXorStep * i),
+                                               k0 * D * 2 + (wave * NI + i) * 1024, 0, 0);
+  };
+
+  // Sᵀ[key][row] of one tile: two 32-key halves, K (A operand) from LDS
+  auto scores = [&](const char* kl, f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            kl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
+      }
+    }
+  };
+  // hide keys a row cannot see; only tiles past the first row's diagonal or
+  // the ragged end need it
+  auto mask = [&](int k0, f32x16_t (&s)[2]) {
+    if (k0 + kBN > mask_from || k0 + kBN > p.Nk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key > lim) s[kb][i] = neg_inf();
+        }
     }
   };
 
@@ -170,50 +214,27 @@ void prefill_bf16_kernel(PrefillParams p) {
   const int tr_row = src >> 2;
   const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
 
-  // one tile: wait for it in `cur`, start the next one into `nxt`, compute
-  auto step = [&](int it, const char* cur, char* nxt) {
+  // One pipeline step for tile `it`, whose scores are in `sc`. K of tile it+1
+  // is in `kn` (its scores are computed here, into `sn`), V of tile it in
+  // `vc`. Loads in flight during the step: K of tile it+2 into `kfree` and V
+  // of tile it+1 into `vfree`.
+  auto step = [&](int it, f32x16_t (&sc)[2], f32x16_t (&sn)[2], const char* kn, const char* vc,
+                  char* kfree, char* vfree) {
     const int k0 = it * kBN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile `it` landed
-    __syncthreads();                     // ... and every other wave's; `nxt` is free again
-    if (it + 1 < ntiles) issue(k0 + kBN, nxt);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it+1) and V(it) have landed
+    __syncthreads();                     // ... for every wave; the free buffers are free
+    if (it + 2 < ntiles) issue(krs, k0 + 2 * kBN, kfree);
+    if (it + 1 < ntiles) issue(vrs, k0 + kBN, vfree);
 
-    const char* kl = cur;
-    const char* vl = cur + TILE;
-
-    // Sᵀ[key][row] for the two 32-key halves of the tile
-    f32x16_t s[2];
+    // tile max of the row (raw scores): four chains of v_maximum3, then
+    // across the halves. (NaN-propagating max: no canonicalisation needed.)
+    float mq[4] = {sc[0][0], sc[0][1], sc[0][2], sc[0][3]};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
+    for (int i = 4; i < 32; i += 4)
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            kl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
-      }
-    }
-
-    // mask: only tiles that reach past the ragged end or the first row's diagonal
-    if (k0 + kBN > mask_from || k0 + kBN > p.Nk) {
-      const long long lim = CAUSAL ? (long long)my_q + p.q_offset : (long long)p.Nk;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool vis = key < p.Nk && (!CAUSAL || key <= lim);
-          if (!vis) s[kb][i] = neg_inf();
-        }
-    }
-
-    // tile max of the row (raw scores), tree-reduced, then across the two halves
-    float mq[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      mq[j] = fmaxf(fmaxf(s[j >> 2][4 * (j & 3)], s[j >> 2][4 * (j & 3) + 1]),
-                    fmaxf(s[j >> 2][4 * (j & 3) + 2], s[j >> 2][4 * (j & 3) + 3]));
-    float mx = fmaxf(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])),
-                     fmaxf(fmaxf(mq[4], mq[5]), fmaxf(mq[6], mq[7])));
+      for (int j = 0; j < 4; ++j) mq[j] = __builtin_elementwise_maximum(mq[j], sc[i >> 4][(i & 15) + j]);
+    float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mq[0], mq[1]),
+                                             __builtin_elementwise_maximum(mq[2], mq[3]));
     mx = max_across_halves(mx);
     const float mt = mx * p.c;
 
@@ -233,6 +254,9 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
     const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
 
+    // scores of the next tile (MFMA) while this tile's exponentials run (VALU)
+    scores(kn, sn);
+
     // P = exp2(s*c - m) in fp32 for the row sum (the LSE needs the unrounded
     // values), P̃ = bf16(P) packed two per dword in Sᵀ register order for PV
     uint32_t pk[2][8];
@@ -241,8 +265,8 @@ void prefill_bf16_kernel(PrefillParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j], p.c, -m_use));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][2 * j + 1], p.c, -m_use));
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][2 * j], p.c, -m_use));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][2 * j + 1], p.c, -m_use));
         ls[(2 * j) & 3] += e0;
         ls[(2 * j + 1) & 3] += e1;
         pk[kb][j] = pack_bf16x2(e0, e1);
@@ -262,9 +286,9 @@ void prefill_bf16_kernel(PrefillParams p) {
         for (int db = 0; db < NDB; ++db) {
           const int col = 32 * db + tr_col;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (ATTN_LDS i16x4_t*)(vl + lds_off<D>(r0, col)));
+              (ATTN_LDS i16x4_t*)(vc + lds_off<D>(r0, col)));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (ATTN_LDS i16x4_t*)(vl + lds_off<D>(r0 + 8, col)));
+              (ATTN_LDS i16x4_t*)(vc + lds_off<D>(r0 + 8, col)));
           const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
           const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -272,12 +296,24 @@ void prefill_bf16_kernel(PrefillParams p) {
                                                             acc[db], 0, 0, 0);
         }
       }
+    mask(k0 + kBN, sn);
   };
 
-  if (ntiles > 0) issue(0, lds0);
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, lds0, lds1);
-    if (it + 1 < ntiles) step(it + 1, lds1, lds0);
+  if (ntiles > 0) {
+    issue(krs, 0, kb0);
+    issue(vrs, 0, vb0);
+    if (ntiles > 1) issue(krs, kBN, kb1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    f32x16_t sa[2], sb[2];
+    scores(kb0, sa);
+    mask(0, sa);
+    // K(1) may still be in flight for other waves: the first step's barrier
+    // orders it; its V(0) wait is already satisfied.
+    for (int it = 0; it < ntiles; it += 2) {
+      step(it, sa, sb, kb1, vb0, kb0, vb1);
+      if (it + 1 < ntiles) step(it + 1, sb, sa, kb0, vb1, kb1, vb0);
+    }
   }
 
   // ---- epilogue: O = Oᵀ/l written once, LSE = ln(sum) + max --------------------
