@@ -60,6 +60,9 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {
   return __builtin_amdgcn_perm(y, x, 0x07060302u);
 }
 
+constexpr float kTau = 8.0f;               // rescale only when a row max grows by more than 2^8
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, 32-bit dword data
+
 // K/V of one 32-key step, in the registers the MFMAs consume.
 template <int D>
 struct StepRegs {
@@ -67,17 +70,28 @@ struct StepRegs {
   u32x4_t vv[2][4];        // 8 d (chunk r16) of keys 16*h2 + 4*g + jj
 };
 
+// One 16-token stretch of one K/V head as a buffer resource whose range ends
+// after its last valid row: loads past it (tokens beyond the sequence, a
+// block outside the pool) return zeros, with no branch per load.
+struct Span {
+  __amdgpu_buffer_rsrc_t k, v;
+  bool ok;  // the stretch has storage (its keys may be visible)
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   constexpr int NC = D / 32;  // MFMAs per 16 keys for Sᵀ (32 d each)
   const int lane = threadIdx.x & 63;
-  // wave-uniform indices live in scalar registers
+  // wave-uniform indices live in scalar registers; the K/V head varies
+  // fastest, so the waves reading one token range run side by side and
+  // together read whole cache rows
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (wid >= p.B * p.Hkv * p.S) return;
-  const int split = wid % p.S;
-  const int bk = wid / p.S;
-  const int b = bk / p.Hkv;
-  const int kvh = bk % p.Hkv;
+  const int kvh = wid % p.Hkv;
+  const int bs = wid / p.Hkv;
+  const int split = bs % p.S;
+  const int b = bs / p.S;
+  const int bk = b * p.Hkv + kvh;
   const int r16 = lane & 15;  // query row (Sᵀ/Oᵀ column) of this lane
   const int g = lane >> 4;    // lane group 0..3
 
@@ -111,33 +125,40 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   float m_run = neg_inf();
   float l_run = 0.f;
 
-  const long long rstride = (long long)p.cv.hkv * D;  // elements between consecutive tokens
-  const __bf16* kbase = p.k + (long long)kvh * D;
-  const __bf16* vbase = p.v + (long long)kvh * D;
-  const bool v_lane = (8 * r16) < D;  // lanes whose 8-wide d chunk exists
+  const int rowb = p.cv.hkv * D * 2;  // bytes between consecutive tokens of one head
+  // loop-invariant lane byte offsets inside a 16-token stretch
+  const int koff = r16 * rowb + 16 * g;         // K: token r16, d = 8*g (+32c via imm)
+  const int voff = (4 * g) * rowb + 16 * r16;   // V: token 4*g (+jj via soffset), chunk r16
 
-  // Every 16-key half of a step is one cache block (chunks start at multiples
-  // of 32); row0 is the element offset of its first token, -1 if invalid.
-  auto load = [&](int k0, const long long row0[2], StepRegs<D>& r) {
+  // The stretch of tokens [t0, t0 + 16) of this head; rows at or past n read as zeros.
+  auto span = [&](int t0) __attribute__((always_inline)) {
+    Span sp;
+    const long long row = cache_row(p.cv, b, t0);
+    const int valid = min(16, n - t0);
+    sp.ok = row >= 0 && valid > 0;
+    const long long base = sp.ok ? row + (long long)kvh * D : 0;
+    const int bytes = sp.ok ? (valid - 1) * rowb + D * 2 : 0;
+    sp.k = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + base), 0, bytes, kBufferFlags);
+    sp.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + base), 0, bytes, kBufferFlags);
+    return sp;
+  };
+
+  auto load = [&](const Span (&sp)[2], StepRegs<D>& r) __attribute__((always_inline)) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const bool ok = row0[h2] >= 0 && (k0 + 16 * h2 + r16) < ke;
-      const __bf16* kp = kbase + row0[h2] + (long long)r16 * rstride + 8 * g;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        r.kf[h2][c] = ok ? *reinterpret_cast<const bf16x8_t*>(kp + 32 * c) : bf16x8_t{};
+        r.kf[h2][c] = __builtin_bit_cast(
+            bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].k, koff + 64 * c, 0, 0));
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int vk = 4 * g + jj;
-        const bool vok = v_lane && row0[h2] >= 0 && (k0 + 16 * h2 + vk) < ke;
-        r.vv[h2][jj] = vok ? *reinterpret_cast<const u32x4_t*>(vbase + row0[h2] +
-                                                               (long long)vk * rstride + 8 * r16)
-                           : u32x4_t{0, 0, 0, 0};
-      }
+      for (int jj = 0; jj < 4; ++jj)
+        r.vv[h2][jj] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].v, voff, jj * rowb, 0));
     }
   };
 
-  auto compute = [&](int k0, const long long row0[2], const StepRegs<D>& r) {
+  auto compute = [&](int k0, const Span (&sp)[2], const StepRegs<D>& r)
+      __attribute__((always_inline)) {
     f32x4_t s[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -152,16 +173,24 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + 16 * h2 + 4 * g + i;
-        const bool vis = row0[h2] >= 0 && key < limit;
-        if (!vis) s[h2][i] = neg_inf();
+        if (!sp[h2].ok || key >= limit) s[h2][i] = neg_inf();
         mx = __builtin_elementwise_maximum(mx, s[h2][i]);
       }
     mx = max_across_rows16(mx);
     mx = max_across_halves(mx);
-    const float m_new = __builtin_elementwise_maximum(m_run, mx * p.c);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    const float mt = mx * p.c;
+    // the reference max only moves (and O, l are rescaled) when the row max
+    // jumps by more than kTau
+    const bool need = mt > m_run + kTau;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? mt : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 from -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+    }
+    const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
     float rs = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -171,9 +200,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
         s[h2][i] = e;
         rs += e;
       }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+    l_run += rs;
 
     // Oᵀ += Vᵀ Pᵀ: key slot j of lane group g is key 16*(j/4) + 4*g + j%4
     const bf16x4_t p0 = __builtin_convertvector(s[0], bf16x4_t);
@@ -200,26 +227,26 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
   // software pipeline: the next step's block lookups and loads are issued
   // before the current step is computed
   StepRegs<D> ra, rb;
-  long long rowa[2], rowb[2];
-  rowa[0] = cache_row(p.cv, b, kb0);
-  rowa[1] = cache_row(p.cv, b, kb0 + 16);
-  load(kb0, rowa, ra);
+  Span sa[2], sb[2];
+  sa[0] = span(kb0);
+  sa[1] = span(kb0 + 16);
+  load(sa, ra);
   for (int k0 = kb0; k0 < ke; k0 += 64) {
     const bool more1 = k0 + 32 < ke;
     if (more1) {
-      rowb[0] = cache_row(p.cv, b, k0 + 32);
-      rowb[1] = cache_row(p.cv, b, k0 + 48);
-      load(k0 + 32, rowb, rb);
+      sb[0] = span(k0 + 32);
+      sb[1] = span(k0 + 48);
+      load(sb, rb);
     }
-    compute(k0, rowa, ra);
+    compute(k0, sa, ra);
     if (!more1) break;
     const bool more2 = k0 + 64 < ke;
     if (more2) {
-      rowa[0] = cache_row(p.cv, b, k0 + 64);
-      rowa[1] = cache_row(p.cv, b, k0 + 80);
-      load(k0 + 64, rowa, ra);
+      sa[0] = span(k0 + 64);
+      sa[1] = span(k0 + 80);
+      load(sa, ra);
     }
-    compute(k0 + 32, rowb, rb);
+    compute(k0 + 32, sb, rb);
   }
 
   // ---- partial result of this chunk --------------------------------------------
