@@ -4,6 +4,7 @@
 // detected before the first launch.
 #include "attn.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -11,10 +12,9 @@
 
 namespace {
 
-constexpr int kSplitKeyAlign = 32;      // keys per step of the decode kernel
-constexpr long long kTargetWaves = 8192; // enough independent waves to fill 256 CUs several times
-constexpr int kMinChunk = 256;
-constexpr int kMaxChunk = 8192;
+constexpr int kWavesPerCu = 4;          // default decode workers per CU (one per SIMD)
+constexpr int kFallbackCus = 256;       // MI355X, when no device can be queried
+constexpr int kMaxWorkers = 1 << 20;
 constexpr int kMaxRows = 16;            // G*Nq rows per decode wave (one 16-wide MFMA)
 
 bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -23,30 +23,34 @@ bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
-struct SplitPlan {
-  int splits;
-  int chunk;
-};
-
-// Keys per chunk: a multiple of 32; by default sized so that B*Hkv*splits
-// waves number about kTargetWaves, within [kMinChunk, kMaxChunk].
-SplitPlan plan_splits(int B, int Hkv, int max_seq_len, int num_splits) {
-  SplitPlan sp;
-  const long long L = max_seq_len > 0 ? max_seq_len : 1;
-  long long chunk;
-  if (num_splits > 0) {
-    chunk = (L + num_splits - 1) / num_splits;
-  } else {
-    const long long work = (long long)B * Hkv * L;
-    chunk = (work + kTargetWaves - 1) / kTargetWaves;
-    if (chunk < kMinChunk) chunk = kMinChunk;
-    if (chunk > kMaxChunk) chunk = kMaxChunk;
+// Default number of decode workers: one per SIMD of the current
+// device (its CU count times kWavesPerCu), cached per device.
+int default_workers() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return kFallbackCus * kWavesPerCu;
   }
-  chunk = (chunk + kSplitKeyAlign - 1) / kSplitKeyAlign * kSplitKeyAlign;
-  if (chunk < kSplitKeyAlign) chunk = kSplitKeyAlign;
-  sp.chunk = (int)chunk;
-  sp.splits = (int)((L + chunk - 1) / chunk);
-  return sp;
+  int w = cache[dev].load(std::memory_order_relaxed);
+  if (w > 0) return w;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = kFallbackCus;
+  }
+  w = cus * kWavesPerCu;
+  cache[dev].store(w, std::memory_order_relaxed);
+  return w;
+}
+
+// Workers actually launched: a whole number (at least one) per K/V head.
+int plan_workers(int num_splits, int Hkv) {
+  int w = num_splits > 0 ? num_splits : default_workers();
+  if (w > kMaxWorkers) w = kMaxWorkers;
+  const int per_head = w / Hkv > 0 ? w / Hkv : 1;
+  return per_head * Hkv;
 }
 
 int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
@@ -57,14 +61,28 @@ int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Nq, int d, int max
   if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (!head_dim_ok(d)) return ATTN_EUNSUPPORTED;
   if ((long long)(Hq / Hkv) * Nq > kMaxRows) return ATTN_EUNSUPPORTED;
+  // one 16-token stretch of a head is addressed with 32-bit byte offsets
+  if ((long long)16 * Hkv * d * 2 > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
   return ATTN_OK;
 }
 
-size_t workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, const SplitPlan& sp) {
+struct WorkspaceLayout {
+  size_t part_lse_off, prefix_off, total;
+};
+
+// [pieces * M * d f32 partial O][pieces * M f32 partial LSE][(B+1) int64 prefix],
+// pieces = workers + B*Hkv (workers a multiple of Hkv); each part 256-byte aligned
+WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int Nq, int d, int workers) {
   const long long M = (long long)(Hq / Hkv) * Nq;
-  const long long rows = (long long)B * Hkv * sp.splits * M;
-  const long long o_bytes = (rows * d * 4 + 255) / 256 * 256;
-  return (size_t)(o_bytes + rows * 4);
+  const long long pieces = (long long)workers + (long long)B * Hkv;
+  auto up = [](long long x) { return (x + 255) / 256 * 256; };
+  WorkspaceLayout l;
+  const long long o_bytes = up(pieces * M * d * 4);
+  const long long lse_bytes = up(pieces * M * 4);
+  l.part_lse_off = (size_t)o_bytes;
+  l.prefix_off = (size_t)(o_bytes + lse_bytes);
+  l.total = (size_t)(o_bytes + lse_bytes + ((long long)B + 1) * 8);
+  return l;
 }
 
 }  // namespace
@@ -107,14 +125,14 @@ int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_le
                            int num_splits) {
   const int st = check_decode_shape(ATTN_BF16, B, Hq, Hkv, Nq, d, max_seq_len, num_splits);
   if (st != ATTN_OK) return st;
-  return plan_splits(B, Hkv, max_seq_len, num_splits).splits;
+  return plan_workers(num_splits, Hkv);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
                                    int num_splits) {
   if (check_decode_shape(ATTN_BF16, B, Hq, Hkv, Nq, d, max_seq_len, num_splits) != ATTN_OK)
     return 0;
-  return workspace_bytes(B, Hq, Hkv, Nq, d, plan_splits(B, Hkv, max_seq_len, num_splits));
+  return workspace_layout(B, Hq, Hkv, Nq, d, plan_workers(num_splits, Hkv)).total;
 }
 
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -134,12 +152,10 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
       (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
       (reinterpret_cast<uintptr_t>(block_table) & 3u))
     return ATTN_EINVAL;
-  const SplitPlan sp = plan_splits(B, Hkv, max_seq_len, num_splits);
-  const size_t need = workspace_bytes(B, Hq, Hkv, Nq, d, sp);
-  if (workspace == nullptr || misaligned16(workspace) || workspace_bytes_given < need)
+  const int workers = plan_workers(num_splits, Hkv);
+  const WorkspaceLayout lay = workspace_layout(B, Hq, Hkv, Nq, d, workers);
+  if (workspace == nullptr || misaligned16(workspace) || workspace_bytes_given < lay.total)
     return ATTN_EWORKSPACE;
-  const long long rows = (long long)B * Hkv * sp.splits * (Hq / Hkv) * Nq;
-  const long long o_bytes = (rows * d * 4 + 255) / 256 * 256;
   attn::DecodeArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -158,10 +174,11 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   a.scale = scale;
   a.causal = causal != 0;
   a.max_seq_len = max_seq_len;
-  a.num_splits = sp.splits;
-  a.chunk = sp.chunk;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  a.workers = workers;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(ws);
+  a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse_off);
+  a.prefix = reinterpret_cast<long long*>(ws + lay.prefix_off);
   return status_of(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -13,23 +13,33 @@
 // Mapping onto CDNA4. Decode reads every K/V byte once and does ~4 flops per
 // byte, so it is bound by HBM bandwidth; the kernel's job is to keep enough
 // bytes in flight and to spend little issue bandwidth per byte.
-//   * One wave per (sequence, K/V head, key chunk). All G·Nq query rows that
-//     share the K/V head (G = Hq/Hkv query heads × Nq new tokens, at most 16)
-//     are the 16 columns of v_mfma_f32_16x16x32_bf16, so every K/V byte is
-//     loaded from HBM once and used by all of them.
+//   * Work split ("stream-K"): per K/V head, the 32-key steps of all
+//     sequences are laid end to end and the head's Wh waves each take an
+//     equal contiguous range of them, so the load stays balanced whatever the
+//     sequence lengths. Wave w serves head w % Hkv, so the waves resident
+//     side by side read the same token rows of every head. A wave writes one
+//     partial result per sequence piece it covers; the piece of the head's
+//     wave j in sequence b lives at index kvh*(Wh + B) + j + b, which is
+//     unique. With fewer steps than waves only the first (number of steps)
+//     waves of a head run.
+//   * All G·Nq query rows that share the K/V head (G = Hq/Hkv query heads ×
+//     Nq new tokens, at most 16) are the 16 columns of
+//     v_mfma_f32_16x16x32_bf16, so every K/V byte is loaded once and used by
+//     all of them.
 //   * Sᵀ = K·Qᵀ: K rows come straight from global memory into the A operand
 //     (lane = key, 8 consecutive d per lane), Qᵀ sits in registers.
 //   * Oᵀ = Vᵀ·Pᵀ: V rows are loaded 16 bytes per lane (8 consecutive d of one
 //     key, a whole 256-byte row per 16 lanes) and transposed in registers with
 //     byte permutes into the A operand, one MFMA per d residue mod 8. Pᵀ is
 //     the Sᵀ accumulator packed to bf16.
-//   * Every 16-key half of a 32-key step is one cache block; its address is
-//     looked up once per step. Keys past seq_len or in invalid blocks are
-//     never loaded (zeros) and are masked, so stale or NaN cache contents
-//     cannot leak into the result.
-//   * Partial results (normalised O and base-2 LSE per chunk and row) go to
-//     the caller's workspace; the combine kernel merges them with weights
-//     exp2(LSE_s - max_s LSE_s) and writes O (bf16) and the natural-log LSE.
+//   * Each 16-token stretch of a head is one buffer resource whose range ends
+//     after its last valid row: tokens past seq_len and blocks outside the
+//     pool read as zeros (and are masked), so stale or NaN cache contents
+//     cannot leak into the result and no load needs a branch.
+//   * Partial results (normalised O and base-2 LSE per piece and row) go to
+//     the caller's workspace; the combine kernel merges the pieces of each
+//     segment in wave order with weights exp2(LSE_s - max LSE_s) and writes O
+//     (bf16) and the natural-log LSE.
 #include "common.h"
 #include "launch.h"
 
@@ -44,12 +54,41 @@ struct DecodeParams {
   const int32_t* seq_lens;
   __bf16* o;
   float* lse;
-  float* part_o;
-  float* part_lse;
-  int B, Hq, Hkv, Nq, G, M, S, chunk;
+  float* part_o;          // [Hkv * (Wh + B) pieces][M][D]
+  float* part_lse;        // [Hkv * (Wh + B) pieces][M]
+  long long* prefix;      // [B + 1]: 32-key steps of sequences 0..b-1
+  int B, Hq, Hkv, Nq, G, M;
+  int W;                  // waves launched: Wh per K/V head
+  int Wh;
   float c;  // scale * log2(e)
   int causal;
 };
+
+// 32-key steps of sequence b (its clamped length rounded up)
+__device__ __forceinline__ int seq_steps(const DecodeParams& p, int b) {
+  return (cache_len_clamped(p.cv, p.seq_lens[b]) + 31) >> 5;
+}
+
+__device__ __forceinline__ long long wave_sum64(long long x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// the wave whose range of steps contains step x: largest w with w*U/W <= x
+__device__ __forceinline__ int wave_of(long long x, long long U, int W) {
+  return (int)(((x + 1) * W - 1) / U);
+}
 
 __device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) {
   // (low 16 bits of x) | (low 16 bits of y) << 16
@@ -79,200 +118,275 @@ struct Span {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_partial_kernel(DecodeParams p) {
   constexpr int NC = D / 32;  // MFMAs per 16 keys for Sᵀ (32 d each)
   const int lane = threadIdx.x & 63;
-  // wave-uniform indices live in scalar registers; the K/V head varies
-  // fastest, so the waves reading one token range run side by side and
-  // together read whole cache rows
-  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (wid >= p.B * p.Hkv * p.S) return;
-  const int kvh = wid % p.Hkv;
-  const int bs = wid / p.Hkv;
-  const int split = bs % p.S;
-  const int b = bs / p.S;
-  const int bk = b * p.Hkv + kvh;
   const int r16 = lane & 15;  // query row (Sᵀ/Oᵀ column) of this lane
   const int g = lane >> 4;    // lane group 0..3
+  // wave-uniform indices live in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (w >= p.W) return;
 
-  const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
-  const int kb0 = split * p.chunk;
-  const int ke = min(n, kb0 + p.chunk);
-  if (kb0 >= ke) return;  // empty chunk: the combine never reads it
-  float* po = p.part_o + ((long long)bk * p.S + split) * p.M * D;
-  float* pl = p.part_lse + ((long long)bk * p.S + split) * p.M;
-
-  // rows r = qi * G + h, r < M
-  const bool row_ok = r16 < p.M;
-  const int qi = row_ok ? r16 / p.G : 0;
-  int limit = ke;  // keys of this chunk visible to the row: [kb0, limit)
-  if (p.causal) limit = min(limit, n - p.Nq + qi + 1);
-
-  // Qᵀ as the B operand: lane holds row r16, d = 32*c + 8*g + j
-  bf16x8_t qf[NC];
-  {
-    const int h = row_ok ? r16 % p.G : 0;
-    const __bf16* qp =
-        p.q + (((long long)b * p.Nq + qi) * p.Hq + (long long)kvh * p.G + h) * D + 8 * g;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qp + 32 * c) : bf16x8_t{};
+  // ---- this wave's range of 32-key steps --------------------------------------
+  // Wave w serves K/V head w % Hkv; the Wh waves of a head split that head's
+  // steps of all sequences laid end to end. Neighbouring waves thus read the
+  // same token rows of different heads.
+  const int kvh = w % p.Hkv;
+  const int j = w / p.Hkv;
+  // Total steps per head; wave 0 also records the per-sequence prefix for the combine.
+  long long tot = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int st = b < p.B ? seq_steps(p, b) : 0;
+    const int incl = wave_scan(st, lane);
+    if (w == 0) {
+      if (b < p.B) p.prefix[b] = tot + incl - st;
+      if (b == p.B - 1) p.prefix[p.B] = tot + incl;
+    }
+    tot += __shfl(incl, 63, 64);
   }
-
-  f32x4_t acc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{};
-  float m_run = neg_inf();
-  float l_run = 0.f;
+  // at most one wave per step, so every wave's range is non-empty and the
+  // pieces of a sequence come from consecutive waves with no gap
+  const int We = (int)min((long long)p.Wh, tot);
+  if (j >= We) return;
+  const long long x0 = (long long)j * tot / We;
+  const long long x1 = (long long)(j + 1) * tot / We;
+  // the sequence holding step x0: first b with prefix[b + 1] > x0
+  int b = 0;
+  long long pb = 0;  // prefix[b]
+  {
+    long long run = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+      const int bb = b0 + lane;
+      const int st = bb < p.B ? seq_steps(p, bb) : 0;
+      const int incl = wave_scan(st, lane);
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(bb < p.B && run + incl > x0);
+      if (hit != 0) {
+        const int l = __builtin_ctzll(hit);
+        b = b0 + l;
+        pb = run + __shfl(incl - st, l, 64);
+        break;
+      }
+      run += __shfl(incl, 63, 64);
+    }
+  }
+  b = __builtin_amdgcn_readfirstlane(b);
 
   const int rowb = p.cv.hkv * D * 2;  // bytes between consecutive tokens of one head
   // loop-invariant lane byte offsets inside a 16-token stretch
   const int koff = r16 * rowb + 16 * g;         // K: token r16, d = 8*g (+32c via imm)
   const int voff = (4 * g) * rowb + 16 * r16;   // V: token 4*g (+jj via soffset), chunk r16
+  const bool row_ok = r16 < p.M;                // rows r = qi * G + h, r < M
+  const int qi = row_ok ? r16 / p.G : 0;
+  const int hrow = row_ok ? r16 % p.G : 0;
 
-  // The stretch of tokens [t0, t0 + 16) of this head; rows at or past n read as zeros.
-  auto span = [&](int t0) __attribute__((always_inline)) {
-    Span sp;
-    const long long row = cache_row(p.cv, b, t0);
-    const int valid = min(16, n - t0);
-    sp.ok = row >= 0 && valid > 0;
-    const long long base = sp.ok ? row + (long long)kvh * D : 0;
-    const int bytes = sp.ok ? (valid - 1) * rowb + D * 2 : 0;
-    sp.k = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + base), 0, bytes, kBufferFlags);
-    sp.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + base), 0, bytes, kBufferFlags);
-    return sp;
-  };
-
-  auto load = [&](const Span (&sp)[2], StepRegs<D>& r) __attribute__((always_inline)) {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        r.kf[h2][c] = __builtin_bit_cast(
-            bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].k, koff + 64 * c, 0, 0));
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        r.vv[h2][jj] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].v, voff, jj * rowb, 0));
-    }
-  };
-
-  auto compute = [&](int k0, const Span (&sp)[2], const StepRegs<D>& r)
+  // ---- one piece: keys [kb0, ke) of head kvh of sequence b ---------------------
+  auto piece = [&](int b, int kvh, int n, int kb0, int ke, long long id)
       __attribute__((always_inline)) {
-    f32x4_t s[2];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      s[h2] = f32x4_t{};
+    float* po = p.part_o + id * p.M * D;
+    float* pl = p.part_lse + id * p.M;
+    int limit = ke;  // keys of this piece visible to the row: [kb0, limit)
+    if (p.causal) limit = min(limit, n - p.Nq + qi + 1);
+
+    // Qᵀ as the B operand: lane holds row r16, d = 32*c + 8*g + j
+    bf16x8_t qf[NC];
+    {
+      const __bf16* qp =
+          p.q + (((long long)b * p.Nq + qi) * p.Hq + (long long)kvh * p.G + hrow) * D + 8 * g;
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.kf[h2][c], qf[c], s[h2], 0, 0, 0);
+        qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qp + 32 * c) : bf16x8_t{};
     }
-    float mx = neg_inf();
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * h2 + 4 * g + i;
-        if (!sp[h2].ok || key >= limit) s[h2][i] = neg_inf();
-        mx = __builtin_elementwise_maximum(mx, s[h2][i]);
-      }
-    mx = max_across_rows16(mx);
-    mx = max_across_halves(mx);
-    const float mt = mx * p.c;
-    // the reference max only moves (and O, l are rescaled) when the row max
-    // jumps by more than kTau
-    const bool need = mt > m_run + kTau;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = need ? mt : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 from -inf
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] *= alpha;
-    }
-    const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h2][i], p.c, -m_use));
-        s[h2][i] = e;
-        rs += e;
-      }
-    l_run += rs;
 
-    // Oᵀ += Vᵀ Pᵀ: key slot j of lane group g is key 16*(j/4) + 4*g + j%4
-    const bf16x4_t p0 = __builtin_convertvector(s[0], bf16x4_t);
-    const bf16x4_t p1 = __builtin_convertvector(s[1], bf16x4_t);
-    const bf16x8_t pb = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    f32x4_t acc[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // dword e of each V chunk holds d = 8*r16 + 2e, 2e+1
-      u32x4_t lo, hi;
-      lo[0] = perm_lo(r.vv[0][0][e], r.vv[0][1][e]);
-      lo[1] = perm_lo(r.vv[0][2][e], r.vv[0][3][e]);
-      lo[2] = perm_lo(r.vv[1][0][e], r.vv[1][1][e]);
-      lo[3] = perm_lo(r.vv[1][2][e], r.vv[1][3][e]);
-      hi[0] = perm_hi(r.vv[0][0][e], r.vv[0][1][e]);
-      hi[1] = perm_hi(r.vv[0][2][e], r.vv[0][3][e]);
-      hi[2] = perm_hi(r.vv[1][0][e], r.vv[1][1][e]);
-      hi[3] = perm_hi(r.vv[1][2][e], r.vv[1][3][e]);
-      acc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo), pb,
-                                                           acc[2 * e], 0, 0, 0);
-      acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
-                                                               pb, acc[2 * e + 1], 0, 0, 0);
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{};
+    float m_run = neg_inf();
+    float l_run = 0.f;
+
+    // Paged: the table entries of 64 consecutive blocks starting at tab_base,
+    // one per lane, fetched with one load and picked with readlane, so a
+    // stretch's K/V loads do not wait on a table load of their own.
+    int tab = -1;
+    int tab_base = -64;
+    // The stretch of tokens [t0, t0 + 16) of this head (t0 a multiple of 16);
+    // rows at or past n read as zeros.
+    auto span = [&](int t0) __attribute__((always_inline)) {
+      Span sp;
+      const int valid = min(16, n - t0);
+      long long row = -1;
+      if (valid > 0) {  // t0 < n, which is within max_len and the table's capacity
+        if (p.cv.table == nullptr) {
+          row = ((long long)b * p.cv.max_len + t0) * p.cv.hkv * D;
+        } else {
+          const int blk = t0 / kBlockTokens;
+          if (blk - tab_base >= 64) {
+            tab_base = blk;
+            const int i = blk + lane;
+            tab = i < p.cv.max_blocks ? p.cv.table[(long long)b * p.cv.max_blocks + i] : -1;
+          }
+          const int e = __builtin_amdgcn_readlane(tab, blk - tab_base);
+          if (e >= 0 && e < p.cv.num_blocks) row = (long long)e * kBlockTokens * p.cv.hkv * D;
+        }
+      }
+      sp.ok = row >= 0;
+      const long long base = sp.ok ? row + (long long)kvh * D : 0;
+      const int bytes = sp.ok ? (valid - 1) * rowb + D * 2 : 0;
+      sp.k = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + base), 0, bytes, kBufferFlags);
+      sp.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + base), 0, bytes, kBufferFlags);
+      return sp;
+    };
+
+    auto load = [&](const Span (&sp)[2], StepRegs<D>& r) __attribute__((always_inline)) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          r.kf[h2][c] = __builtin_bit_cast(
+              bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].k, koff + 64 * c, 0, 0));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          r.vv[h2][jj] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].v, voff, jj * rowb, 0));
+      }
+    };
+
+    auto compute = [&](int k0, const Span (&sp)[2], const StepRegs<D>& r)
+        __attribute__((always_inline)) {
+      f32x4_t s[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        s[h2] = f32x4_t{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.kf[h2][c], qf[c], s[h2], 0, 0, 0);
+      }
+      float mx = neg_inf();
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * h2 + 4 * g + i;
+          if (!sp[h2].ok || key >= limit) s[h2][i] = neg_inf();
+          mx = __builtin_elementwise_maximum(mx, s[h2][i]);
+        }
+      mx = max_across_rows16(mx);
+      mx = max_across_halves(mx);
+      const float mt = mx * p.c;
+      // the reference max only moves (and O, l are rescaled) when the row max
+      // jumps by more than kTau
+      const bool need = mt > m_run + kTau;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 from -inf
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] *= alpha;
+      }
+      const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+      float rs = 0.f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h2][i], p.c, -m_use));
+          s[h2][i] = e;
+          rs += e;
+        }
+      l_run += rs;
+
+      // Oᵀ += Vᵀ Pᵀ: key slot j of lane group g is key 16*(j/4) + 4*g + j%4
+      const bf16x4_t p0 = __builtin_convertvector(s[0], bf16x4_t);
+      const bf16x4_t p1 = __builtin_convertvector(s[1], bf16x4_t);
+      const bf16x8_t pb8 = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // dword e of each V chunk holds d = 8*r16 + 2e, 2e+1
+        u32x4_t lo, hi;
+        lo[0] = perm_lo(r.vv[0][0][e], r.vv[0][1][e]);
+        lo[1] = perm_lo(r.vv[0][2][e], r.vv[0][3][e]);
+        lo[2] = perm_lo(r.vv[1][0][e], r.vv[1][1][e]);
+        lo[3] = perm_lo(r.vv[1][2][e], r.vv[1][3][e]);
+        hi[0] = perm_hi(r.vv[0][0][e], r.vv[0][1][e]);
+        hi[1] = perm_hi(r.vv[0][2][e], r.vv[0][3][e]);
+        hi[2] = perm_hi(r.vv[1][0][e], r.vv[1][1][e]);
+        hi[3] = perm_hi(r.vv[1][2][e], r.vv[1][3][e]);
+        acc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo),
+                                                             pb8, acc[2 * e], 0, 0, 0);
+        acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
+                                                                 pb8, acc[2 * e + 1], 0, 0, 0);
+      }
+    };
+
+    // software pipeline: the next step's block lookups and loads are issued
+    // before the current step is computed
+    StepRegs<D> ra, rb;
+    Span sa[2], sb[2];
+    sa[0] = span(kb0);
+    sa[1] = span(kb0 + 16);
+    load(sa, ra);
+    for (int k0 = kb0; k0 < ke; k0 += 64) {
+      const bool more1 = k0 + 32 < ke;
+      if (more1) {
+        sb[0] = span(k0 + 32);
+        sb[1] = span(k0 + 48);
+        load(sb, rb);
+      }
+      compute(k0, sa, ra);
+      if (!more1) break;
+      const bool more2 = k0 + 64 < ke;
+      if (more2) {
+        sa[0] = span(k0 + 64);
+        sa[1] = span(k0 + 80);
+        load(sa, ra);
+      }
+      compute(k0 + 32, sb, rb);
+    }
+
+    // partial result of this piece
+    float l_tot = sum_across_rows16(l_run);
+    l_tot = sum_across_halves(l_tot);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row_ok) {
+      // Oᵀ element (m = 4*g + i, c) is d = 8*m + c = 32*g + 8*i + c
+      if (32 * g < D) {
+        float* dst = po + (long long)r16 * D + 32 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4_t a = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
+          f32x4_t bq = {acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv};
+          *reinterpret_cast<f32x4_t*>(dst + 8 * i) = a;
+          *reinterpret_cast<f32x4_t*>(dst + 8 * i + 4) = bq;
+        }
+      }
+      if (g == 0) pl[r16] = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : neg_inf();
     }
   };
 
-  // software pipeline: the next step's block lookups and loads are issued
-  // before the current step is computed
-  StepRegs<D> ra, rb;
-  Span sa[2], sb[2];
-  sa[0] = span(kb0);
-  sa[1] = span(kb0 + 16);
-  load(sa, ra);
-  for (int k0 = kb0; k0 < ke; k0 += 64) {
-    const bool more1 = k0 + 32 < ke;
-    if (more1) {
-      sb[0] = span(k0 + 32);
-      sb[1] = span(k0 + 48);
-      load(sb, rb);
-    }
-    compute(k0, sa, ra);
-    if (!more1) break;
-    const bool more2 = k0 + 64 < ke;
-    if (more2) {
-      sa[0] = span(k0 + 64);
-      sa[1] = span(k0 + 80);
-      load(sa, ra);
-    }
-    compute(k0 + 32, sb, rb);
-  }
-
-  // ---- partial result of this chunk --------------------------------------------
-  float l_tot = sum_across_rows16(l_run);
-  l_tot = sum_across_halves(l_tot);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (row_ok) {
-    // Oᵀ element (m = 4*g + i, c) is d = 8*m + c = 32*g + 8*i + c
-    if (32 * g < D) {
-      float* dst = po + (long long)r16 * D + 32 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4_t a = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
-        f32x4_t bq = {acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv};
-        *reinterpret_cast<f32x4_t*>(dst + 8 * i) = a;
-        *reinterpret_cast<f32x4_t*>(dst + 8 * i + 4) = bq;
-      }
-    }
-    if (g == 0) pl[r16] = l_tot > 0.f ? m_run + __builtin_amdgcn_logf(l_tot) : neg_inf();
+  // ---- walk the sequences that [x0, x1) covers ---------------------------------
+  int st_b = seq_steps(p, b);
+  long long seg = pb;  // first step of sequence b
+  long long x = x0;
+  while (x < x1) {
+    const int lo = (int)(x - seg);
+    const int hi = (int)min((long long)st_b, x1 - seg);
+    const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
+    piece(b, kvh, n, 32 * lo, min(n, 32 * hi), (long long)kvh * (p.Wh + p.B) + j + b);
+    x = seg + hi;
+    seg += st_b;
+    do {
+      ++b;
+      st_b = b < p.B ? seq_steps(p, b) : 1;
+    } while (b < p.B && st_b == 0);
   }
 }
 
-// One workgroup of 4 waves per (sequence, K/V head, query row). Wave w merges
-// the chunks s = w, w+4, ... with weights exp2(LSE_s - max); the four partial
-// sums are added in a fixed order through LDS, so the result is deterministic.
-// Each lane owns D/64 consecutive output elements.
+// One workgroup of 4 waves per (sequence, K/V head, query row). The pieces of
+// sequence b for head kvh were written by that head's waves w_first..w_last
+// at index kvh*(Wh + B) + b + j; wave i of the workgroup merges the pieces
+// w_first + i, + 4, ... with weights exp2(LSE - max LSE), and the four
+// partial sums are added in a fixed order through LDS, so the result is
+// deterministic. Each lane owns D/64 consecutive output elements.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   constexpr int E = D / 64;  // elements per lane
@@ -286,43 +400,52 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
   const int kvh = bk % p.Hkv;
   const int qi = r / p.G;
   const int hq = kvh * p.G + r % p.G;
-  const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
-  const int used = min(p.S, (n + p.chunk - 1) / p.chunk);
-  const float* pl = p.part_lse + (long long)bk * p.S * p.M + r;
-  const float* po = p.part_o + ((long long)bk * p.S * p.M + r) * D + E * lane;
+  const long long T = p.prefix[p.B];  // steps per head
+  const int We = (int)min((long long)p.Wh, T);  // waves per head that took a range
+  const int st_b = seq_steps(p, b);
+  int w_first = 0, w_last = -1;
+  if (st_b > 0) {
+    w_first = wave_of(p.prefix[b], T, We);
+    w_last = wave_of(p.prefix[b] + st_b - 1, T, We);
+  }
+  const long long first = (long long)kvh * (p.Wh + p.B) + b + w_first;
+  const float* pl = p.part_lse + first * p.M + r;
+  const float* po = p.part_o + (first * p.M + r) * D + E * lane;
+  const int used = w_last - w_first + 1;
 
   float mx = neg_inf();
-  for (int s = 0; s < used; ++s) mx = fmaxf(mx, pl[(long long)s * p.M]);
+  for (int i = 0; i < used; ++i)
+    mx = __builtin_elementwise_maximum(mx, pl[(long long)i * p.M]);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float tot = 0.f;
   if (mx != neg_inf()) {
-    int s = wave;
-    for (; s + 12 < used; s += 16) {  // four chunks in flight per lane
-      float w[4];
+    int i = wave;
+    for (; i + 12 < used; i += 16) {  // four pieces in flight per lane
+      float wt[4];
       float v[4][E];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float ls = pl[(long long)(s + 4 * u) * p.M];
-        w[u] = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
+        const float ls = pl[(long long)(i + 4 * u) * p.M];
+        wt[u] = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[u][e] = po[(long long)(s + 4 * u) * p.M * D + e];
+        for (int e = 0; e < E; ++e) v[u][e] = po[(long long)(i + 4 * u) * p.M * D + e];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        tot += w[u];
+        tot += wt[u];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(w[u], v[u][e], acc[e]);
+        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wt[u], v[u][e], acc[e]);
       }
     }
-    for (; s < used; s += 4) {
-      const float ls = pl[(long long)s * p.M];
-      const float w = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
-      tot += w;
+    for (; i < used; i += 4) {
+      const float ls = pl[(long long)i * p.M];
+      const float wt = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
+      tot += wt;
 #pragma unroll
       for (int e = 0; e < E; ++e)
-        acc[e] = __builtin_fmaf(w, po[(long long)s * p.M * D + e], acc[e]);
+        acc[e] = __builtin_fmaf(wt, po[(long long)i * p.M * D + e], acc[e]);
     }
   }
 #pragma unroll
@@ -363,19 +486,19 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   pp.lse = a.lse;
   pp.part_o = a.part_o;
   pp.part_lse = a.part_lse;
+  pp.prefix = a.prefix;
   pp.B = a.B;
   pp.Hq = a.Hq;
   pp.Hkv = a.Hkv;
   pp.Nq = a.Nq;
   pp.G = a.Hq / a.Hkv;
   pp.M = pp.G * a.Nq;
-  pp.S = a.num_splits;
-  pp.chunk = a.chunk;
+  pp.Wh = a.workers / a.Hkv;
+  pp.W = pp.Wh * a.Hkv;
   pp.c = a.scale * kLog2e;
   pp.causal = a.causal;
-  const long long waves = (long long)a.B * a.Hkv * pp.S;
-  if (waves <= 0) return hipSuccess;
-  const long long blocks = (waves + 3) / 4;
+  if (a.B <= 0 || pp.Wh <= 0) return hipSuccess;
+  const long long blocks = (pp.W + 3) / 4;
   const long long cblocks = (long long)a.B * a.Hkv * pp.M;
   if (blocks > 0x7fffffffLL || cblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.d == 128) {

@@ -35,10 +35,10 @@ struct DecodeArgs {
   float scale;
   int causal;
   int max_seq_len;
-  int num_splits;
-  int chunk;  // keys per split, a multiple of 32
-  float* part_o;    // [B*Hkv*num_splits*M, d]
-  float* part_lse;  // [B*Hkv*num_splits*M]
+  int workers;        // waves sharing the key space
+  float* part_o;      // [(workers + B*Hkv) * M, d]
+  float* part_lse;    // [(workers + B*Hkv) * M]
+  long long* prefix;  // [B + 1]
 };
 
 struct CacheCopyArgs {

@@ -98,14 +98,25 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
  *                 causal it sees keys j <= that position ("Effizienz",
  *                 "Der wichtige Maskenfehler beim Cache"), without causal all
  *                 seq_lens[b] keys.
- *   max_seq_len : an upper bound of seq_lens; it sizes the split grid.
- *                 Device-side, seq_lens[b] is clamped to [0, max_seq_len]
- *                 (and to max_blocks_per_seq·16 when paged). Table entries
- *                 outside [0, num_blocks) make their 16 keys invisible.
- *   num_splits  : key chunks per (sequence, K/V head); 0 picks a default.
+ *   max_seq_len : an upper bound of seq_lens. Device-side, seq_lens[b] is
+ *                 clamped to [0, max_seq_len] (and to max_blocks_per_seq·16
+ *                 when paged). Table entries outside [0, num_blocks) make
+ *                 their 16 keys invisible.
+ *   num_splits  : number of workers (GPU waves) that share the keys, rounded
+ *                 down to a multiple of Hkv (at least Hkv). Each K/V head gets
+ *                 num_splits/Hkv workers; the head's 32-key steps of all
+ *                 sequences are laid end to end and cut into that many equal
+ *                 ranges, so the split adapts to ragged lengths. 0 picks a
+ *                 default for the current device (a few per compute unit).
  *   workspace   : device scratch of at least attn_decode_workspace_bytes()
- *                 bytes for the same arguments; it holds each chunk's partial
- *                 output and LSE between the partial and combine kernels.
+ *                 bytes for the same arguments, owned by the caller and
+ *                 free again once the call's work on `stream` is done. It
+ *                 holds the partial output and LSE of every piece (one per
+ *                 worker and sequence it touches, at most
+ *                 workers + B·Hkv of them) and a [B + 1] int64 prefix sum
+ *                 of per-sequence step counts, all written before they are
+ *                 read, so it needs no clearing. Calls that share one
+ *                 workspace must be ordered on one stream.
  * Supported: dtype ATTN_BF16, d in {64, 128}, (Hq/Hkv)·Nq <= 16.
  */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -115,8 +126,8 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       float scale, int causal, int max_seq_len, int num_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Split count attn_decode_paged uses for these arguments (num_splits = 0:
- * the default), or a negative attn_status. */
+/* Worker count attn_decode_paged uses for these arguments (num_splits = 0:
+ * the default for the current device), or a negative attn_status. */
 int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
                            int num_splits);
 

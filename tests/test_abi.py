@@ -116,16 +116,22 @@ def test_decode_rejects(kw, code):
     assert _decode(**kw) == code
 
 
-def test_split_plan_and_workspace_size():
+def test_worker_plan_and_workspace_size():
     lib = eta.library()
-    # 16 sequences x 8 K/V heads x 32768 keys: 512-key chunks, 64 splits
-    assert lib.attn_decode_num_splits(16, 32, 8, 1, 128, 32768, 0) == 64
-    assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 100, 0) == 1
-    assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 1000, 3) == 3
+    # default: a few workers per CU (256 CUs when no device can be queried,
+    # as here); an explicit count is rounded down to a multiple of Hkv
+    w = lib.attn_decode_num_splits(16, 32, 8, 1, 128, 32768, 0)
+    assert w > 0 and w % 8 == 0
+    assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 100, 3) == 8
+    assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 100, 20) == 16
+    assert lib.attn_decode_num_splits(1, 32, 2, 1, 128, 100, 7) == 6
     assert lib.attn_decode_num_splits(1, 32, 8, 5, 128, 1000, 0) == eta.ATTN_EUNSUPPORTED
-    # rows = B*Hkv*splits*G*Nq; O partials f32 (256-byte padded) then f32 LSE per row
-    rows = 16 * 8 * 64 * 4
-    assert lib.attn_decode_workspace_bytes(16, 32, 8, 1, 128, 32768, 0) == rows * 128 * 4 + rows * 4
+    # pieces = workers + B*Hkv; [pieces*M*d f32][pieces*M f32][(B+1) int64], 256-byte aligned
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    pieces = 96 + 16 * 8  # 100 requested -> 12 per K/V head
+    M = 4
+    want = up(pieces * M * 128 * 4) + up(pieces * M * 4) + 17 * 8
+    assert lib.attn_decode_workspace_bytes(16, 32, 8, 1, 128, 32768, 100) == want
     assert lib.attn_decode_workspace_bytes(16, 32, 8, 9, 128, 32768, 0) == 0
 
 

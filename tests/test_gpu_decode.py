@@ -187,3 +187,23 @@ def test_paged_decode_q4_workload_sampled():
             O, L = oracle.attention_rows(inp["q"][b, :, hq].cpu(), n - 4 + np.arange(4),
                                          K[:, hq // G], V[:, hq // G], scale_of(w["d"]), True)
             check(o[b, :, hq], O, lse[b, hq], L, "bf16", f"b={b} hq={hq}")
+
+
+@pytest.mark.parametrize("workers", [1, 2, 5, 13, 64, 1000])
+def test_worker_split_boundaries_with_empty_sequences(workers):
+    """Key steps of all (sequence, K/V head) segments are shared out evenly among
+    the workers, so pieces start and end inside and across segments. Empty
+    sequences contribute no steps; a workspace full of NaN shows any read of a
+    piece that no worker wrote."""
+    dev = need_gpu()
+    lens = [0, 70, 1, 0, 33, 300, 16, 0]
+    announce(f"contiguous decode, workers={workers}, lens={lens}, NaN-filled workspace")
+    B, Hq, Hkv, Nq, d, L = len(lens), 8, 2, 1, 128, 320
+    q, kc, vc, sl = inputs.decode_contig_inputs(26, B, Hq, Hkv, Nq, d, L, lens)
+    need = eta.attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, L, workers)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev)
+    o, lse = eta.attn_decode_paged(q.to(dev), kc.to(dev), vc.to(dev), sl.to(dev), causal=True,
+                                   num_splits=workers, workspace=ws)
+    torch.cuda.synchronize()
+    O, Lr = oracle.decode_attention(q, kc, vc, sl, scale_of(d), True)
+    check(o, O, lse, Lr, "bf16", f"workers={workers}")
