@@ -121,8 +121,38 @@ class StageTimer:
         return sum(a.elapsed_time(b) for a, b in ps) / len(ps)
 
 
-def cpu_baseline(q, k, v, heads):
-    """Time the fp64 oracle on `heads` of the 4k causal prefill (all rows)."""
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters_all_workloads.md")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc")
+
+
+def counter_traffic(stage, kernel, sources):
+    """HBM bytes per launch of `kernel` on `stage` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy calibration), or None
+    when the kernel's sources have changed since the counters were taken."""
+    import hashlib
+
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    fp = h.hexdigest()[:16]
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) < 4 or parts[0] != "traffic" or parts[1] != stage or parts[2] != kernel:
+                continue
+            kv = dict(x.split("=", 1) for x in parts[3:] if "=" in x)
+            if kv.get("sources_sha256") != fp:
+                return None
+            return int(kv["bytes_per_launch"])
+    return None
+
+
+def cpu_baseline(q, k, v, min_seconds=10.0, max_heads=64):
+    """Time the fp64 oracle on whole heads (all 4096 rows) of the 4k causal prefill,
+    cycling over the 32 heads until about `min_seconds` of CPU work is done."""
     import numpy as np
 
     import oracle
@@ -138,16 +168,21 @@ def cpu_baseline(q, k, v, heads):
     vc = v.cpu()
     d = q.shape[-1]
     G = q.shape[1] // k.shape[1]
+    Hq = q.shape[1]
+    done = 0
     t0 = time.perf_counter()
-    for hq in heads:
+    while done < max_heads and (done < 1 or time.perf_counter() - t0 < min_seconds):
+        hq = done % Hq
         oracle.attention_rows(qc[0, hq], np.arange(q.shape[2]), kc[0, hq // G], vc[0, hq // G],
                               1.0 / math.sqrt(d), True)
+        done += 1
     dt = time.perf_counter() - t0
-    flops = prefill_flops(1, len(heads), q.shape[2], d)
+    flops = prefill_flops(1, done, q.shape[2], d)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{len(heads)} of 32 heads, all 4096 rows, of the causal GQA 4k prefill "
-                      f"(fp64 numpy, {dt:.1f} s)"}
+            "sample": f"{done} head passes (heads taken in order, cycling over the {Hq}), all "
+                      f"{q.shape[2]} rows each, of the causal GQA 4k prefill (fp64 numpy, "
+                      f"{dt:.1f} s)"}
 
 
 def main():
@@ -240,11 +275,15 @@ def main():
     result_workloads["splitkv_decode_32k"] = {
         "ms": round(ms4, 5), "GB/s": round(bytes4 / (ms4 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "kv_bytes": bytes4}
+        "kv_bytes": bytes4,
+        "traffic_partial_kernel": counter_traffic("splitkv_decode_32k", "decode_partial_kernel<128>",
+                                                  ["common.h", "decode.hip"])}
     result_workloads["paged_decode_q4"] = {
         "ms": round(ms5, 5), "GB/s": round(bytes5 / (ms5 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes5 / (ms5 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-        "kv_bytes": bytes5, "kv_append_ms": round(msa, 5)}
+        "kv_bytes": bytes5, "kv_append_ms": round(msa, 5),
+        "traffic_partial_kernel": counter_traffic("paged_decode_q4", "decode_partial_kernel<128>",
+                                                  ["common.h", "decode.hip"])}
 
     # long-context prefill and the fp32 single-head case, in their own loops
     print("[bench] long-context prefill", file=sys.stderr, flush=True)
@@ -273,15 +312,18 @@ def main():
     torch.cuda.synchronize()
     result_workloads["single_head_f32"] = {"us": round(t1.mean_ms("p") * 1e3, 2)}
 
+    traffic = counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true>",
+                              ["common.h", "prefill_bf16.hip"])
     roofline = {"bound": "mfma", "achieved": round(tflops2, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops2 / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "kernel": "prefill_bf16_kernel<128, causal>",
+                "traffic": traffic, "traffic_unit": "bytes per launch (HBM read + write)",
+                "kernel": "prefill_bf16_kernel<128, causal>",
                 "per_launch": f"{flops2:.6g} FLOP (visible pairs x 4d) per launch"}
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(q2, k2, v2, heads=list(range(8)))
+        cpu = cpu_baseline(q2, k2, v2)
         cpu["host"] = platform.processor() or platform.machine()
         cpu["host_cpus"] = os.cpu_count()
 

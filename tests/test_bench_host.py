@@ -1,0 +1,39 @@
+"""Host-side checks of bench.py: the one-GPU contract, the FLOP count and the
+counter-traffic lookup (no GPU needed)."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_causal_pair_count_matches_the_oracle_mask():
+    for nq, nk, off in ((1, 1, 0), (7, 7, 0), (5, 9, 4), (9, 5, -4), (64, 300, 236)):
+        # brute force: row i (position i + off) sees keys j <= i + off
+        mask = np.arange(nk)[None, :] <= np.arange(nq)[:, None] + off
+        assert bench.causal_pairs(nq, nk, off) == int(mask.sum())
+        assert bench.causal_pairs(nq, nk, off) == oracle.visible_pairs(nq, nk, True, off)
+    # 4k causal prefill: N(N+1)/2 pairs per head, 4d flops per pair
+    assert bench.prefill_flops(1, 32, 4096, 128) == 4.0 * 128 * 32 * 4096 * 4097 / 2
+
+
+def test_counter_traffic_is_null_for_other_sources():
+    got = bench.counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true>",
+                                ["common.h", "prefill_bf16.hip"])
+    assert got is None or (isinstance(got, int) and got > 0)
+    assert bench.counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true>",
+                                 ["common.h", "kv_cache.hip"]) is None
+    assert bench.counter_traffic("no_such_stage", "x", ["common.h"]) is None
