@@ -10,10 +10,32 @@
 
 #include "launch.h"
 
+namespace attn {
+
+int device_compute_units() {
+  constexpr int kFallbackCus = 256;  // MI355X, when no device can be queried
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return kFallbackCus;
+  }
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return kFallbackCus;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace attn
+
 namespace {
 
 constexpr int kWavesPerCu = 4;          // default decode workers per CU (one per SIMD)
-constexpr int kFallbackCus = 256;       // MI355X, when no device can be queried
 constexpr int kMaxWorkers = 1 << 20;
 constexpr int kMaxRows = 16;            // G*Nq rows per decode wave (one 16-wide MFMA)
 
@@ -23,27 +45,8 @@ bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
-// Default number of decode workers: one per SIMD of the current
-// device (its CU count times kWavesPerCu), cached per device.
-int default_workers() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipGetLastError();
-    return kFallbackCus * kWavesPerCu;
-  }
-  int w = cache[dev].load(std::memory_order_relaxed);
-  if (w > 0) return w;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0) {
-    (void)hipGetLastError();
-    cus = kFallbackCus;
-  }
-  w = cus * kWavesPerCu;
-  cache[dev].store(w, std::memory_order_relaxed);
-  return w;
-}
+// Default number of decode workers: one per SIMD of the current device.
+int default_workers() { return attn::device_compute_units() * kWavesPerCu; }
 
 // Workers actually launched: a whole number (at least one) per K/V head.
 int plan_workers(int num_splits, int Hkv) {

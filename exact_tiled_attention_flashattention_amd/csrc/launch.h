@@ -55,6 +55,10 @@ struct CacheCopyArgs {
   int max_seq_len;
 };
 
+// Compute units of the current device (cached per device; 256 when none can
+// be queried).
+int device_compute_units();
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);

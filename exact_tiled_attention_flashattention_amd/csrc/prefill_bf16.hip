@@ -28,8 +28,14 @@
 //   * Causal workgroups are launched longest-first (highest query block
 //     first) and skip every tile past their last row's diagonal; only tiles
 //     that cross the diagonal or the ragged end of K are masked.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
+
+#ifndef ATTN_PREFILL_SCHED
+#define ATTN_PREFILL_SCHED 0
+#endif
 
 namespace attn {
 namespace {
@@ -188,18 +194,17 @@ void prefill_bf16_kernel(PrefillParams p) {
       }
     }
   };
-  // hide keys a row cannot see; only tiles past the first row's diagonal or
-  // the ragged end need it
-  auto mask = [&](int k0, f32x16_t (&s)[2]) {
-    if (k0 + kBN > mask_from || k0 + kBN > p.Nk) {
+  // only tiles past the first row's diagonal or the ragged end hide keys
+  auto needs_mask = [&](int k0) { return k0 + kBN > mask_from || k0 + kBN > p.Nk; };
+  // hide the keys a row cannot see
+  auto mask = [&](int k0, f32x16_t (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key > lim) s[kb][i] = neg_inf();
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key > lim) s[kb][i] = neg_inf();
+      }
   };
 
   f32x16_t acc[NDB];
@@ -214,29 +219,45 @@ void prefill_bf16_kernel(PrefillParams p) {
   const int tr_row = src >> 2;
   const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
 
-  // One pipeline step for tile `it`, whose scores are in `sc`. K of tile it+1
-  // is in `kn` (its scores are computed here, into `sn`), V of tile it in
-  // `vc`. Loads in flight during the step: K of tile it+2 into `kfree` and V
-  // of tile it+1 into `vfree`.
-  auto step = [&](int it, f32x16_t (&sc)[2], f32x16_t (&sn)[2], const char* kn, const char* vc,
-                  char* kfree, char* vfree) {
-    const int k0 = it * kBN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it+1) and V(it) have landed
-    __syncthreads();                     // ... for every wave; the free buffers are free
-    if (it + 2 < ntiles) issue(krs, k0 + 2 * kBN, kfree);
-    if (it + 1 < ntiles) issue(vrs, k0 + kBN, vfree);
-
-    // tile max of the row (raw scores): four chains of v_maximum3, then
-    // across the halves. (NaN-propagating max: no canonicalisation needed.)
-    float mq[4] = {sc[0][0], sc[0][1], sc[0][2], sc[0][3]};
+  // max over a tile's scores of this lane's row (raw scores): four chains of
+  // v_maximum3, then across the halves, scaled to base 2. (NaN-propagating
+  // max: no canonicalisation needed.)
+  auto tile_max = [&](const f32x16_t (&s)[2]) __attribute__((always_inline)) {
+    float mq[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
     for (int i = 4; i < 32; i += 4)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mq[j] = __builtin_elementwise_maximum(mq[j], sc[i >> 4][(i & 15) + j]);
+      for (int j = 0; j < 4; ++j) mq[j] = __builtin_elementwise_maximum(mq[j], s[i >> 4][(i & 15) + j]);
     float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mq[0], mq[1]),
                                              __builtin_elementwise_maximum(mq[2], mq[3]));
-    mx = max_across_halves(mx);
-    const float mt = mx * p.c;
+    return max_across_halves(mx) * p.c;
+  };
+
+  // One pipeline step for tile `it`, whose unmasked scores are in `sc` and
+  // their row max (base 2) in `mt`. K of tile it+1 is in `kn`, V of tile it in `vc`.
+  // Loads in flight during the step: K of tile it+2 into `kfree` and V of
+  // tile it+1 into `vfree`. The step has two MFMA phases, each paired with
+  // VALU work that does not depend on it:
+  //   1. Sᵀ of tile it+1 (into `sn`)  ||  P = exp2(s*c - m) and row sum of tile it
+  //   2. Oᵀ += Vᵀ Pᵀ of tile it       ||  max of tile it+1 (unmasked)
+  // A tile that hides keys is masked, and its max recomputed, at the start of
+  // its own step, so no branch separates the two phases. On the last tile
+  // (LAST) there is no next tile: phase 1 has no MFMAs.
+  auto step = [&](auto last_tag, int it, f32x16_t (&sc)[2], f32x16_t (&sn)[2], float& mt,
+                  const char* kn, const char* vc, char* kfree, char* vfree)
+      __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int k0 = it * kBN;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it+1) and V(it) have landed
+    __syncthreads();                     // ... for every wave; the free buffers are free
+    if (!LAST) {
+      if (it + 2 < ntiles) issue(krs, k0 + 2 * kBN, kfree);
+      issue(vrs, k0 + kBN, vfree);
+    }
+    if (needs_mask(k0)) {
+      mask(k0, sc);
+      mt = tile_max(sc);
+    }
 
     // online softmax with a lazily moved reference: exp2(s*c - m) stays below
     // 2^kTau, so the reference only moves (and O, l are rescaled) when the
@@ -254,9 +275,8 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
     const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
 
-    // scores of the next tile (MFMA) while this tile's exponentials run (VALU)
-    scores(kn, sn);
-
+    // ---- phase 1 ----
+    if (!LAST) scores(kn, sn);
     // P = exp2(s*c - m) in fp32 for the row sum (the LSE needs the unrounded
     // values), P̃ = bf16(P) packed two per dword in Sᵀ register order for PV
     uint32_t pk[2][8];
@@ -272,8 +292,21 @@ void prefill_bf16_kernel(PrefillParams p) {
         pk[kb][j] = pack_bf16x2(e0, e1);
       }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#if ATTN_PREFILL_SCHED
+    if (!LAST) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+    }
+#endif
 
-    // Oᵀ += Vᵀ Pᵀ, 16 keys per MFMA; Vᵀ via transposing LDS reads
+    // ---- phase 2: Oᵀ += Vᵀ Pᵀ, 16 keys per MFMA; Vᵀ via transposing LDS reads ----
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -296,7 +329,17 @@ void prefill_bf16_kernel(PrefillParams p) {
                                                             acc[db], 0, 0, 0);
         }
       }
-    mask(k0 + kBN, sn);
+    if (!LAST) mt = tile_max(sn);
+#if ATTN_PREFILL_SCHED
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
+    }
+#endif
   };
 
   if (ntiles > 0) {
@@ -307,12 +350,21 @@ void prefill_bf16_kernel(PrefillParams p) {
     __syncthreads();
     f32x16_t sa[2], sb[2];
     scores(kb0, sa);
-    mask(0, sa);
+    float mt = tile_max(sa);
     // K(1) may still be in flight for other waves: the first step's barrier
     // orders it; its V(0) wait is already satisfied.
-    for (int it = 0; it < ntiles; it += 2) {
-      step(it, sa, sb, kb1, vb0, kb0, vb1);
-      if (it + 1 < ntiles) step(it + 1, sb, sa, kb0, vb1, kb1, vb0);
+    using more_t = std::integral_constant<bool, false>;
+    using last_t = std::integral_constant<bool, true>;
+    int it = 0;
+    for (; it + 2 < ntiles; it += 2) {
+      step(more_t{}, it, sa, sb, mt, kb1, vb0, kb0, vb1);
+      step(more_t{}, it + 1, sb, sa, mt, kb0, vb1, kb1, vb0);
+    }
+    if (it + 1 < ntiles) {
+      step(more_t{}, it, sa, sb, mt, kb1, vb0, kb0, vb1);
+      step(last_t{}, it + 1, sb, sa, mt, kb0, vb1, kb1, vb0);
+    } else {
+      step(last_t{}, it, sa, sb, mt, kb1, vb0, kb0, vb1);
     }
   }
 
