@@ -37,7 +37,7 @@ namespace {
 
 constexpr int kWavesPerCu = 4;          // default decode workers per CU (one per SIMD)
 constexpr int kMaxWorkers = 1 << 20;
-constexpr int kMaxRows = 16;            // G*Nq rows per decode wave (one 16-wide MFMA)
+constexpr int kMaxRows = 64;            // G*Nq rows per K/V head (four groups of 16)
 
 bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -48,12 +48,22 @@ int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 // Default number of decode workers: one per SIMD of the current device.
 int default_workers() { return attn::device_compute_units() * kWavesPerCu; }
 
-// Workers actually launched: a whole number (at least one) per K/V head.
-int plan_workers(int num_splits, int Hkv) {
+// Query rows that share a K/V head, and the (K/V head, group of up to 16
+// rows) pairs the decode kernel spreads its workers over (at least Hkv).
+long long decode_rows(int Hq, int Hkv, int Nq) { return (long long)(Hq / Hkv) * Nq; }
+int virtual_heads(int Hq, int Hkv, int Nq) {
+  const long long M = decode_rows(Hq, Hkv, Nq);
+  return Hkv * (M > 16 ? (int)((M + 15) / 16) : 1);
+}
+
+// Workers actually launched: a whole number (at least one) per (K/V head,
+// row group).
+int plan_workers(int num_splits, int Hq, int Hkv, int Nq) {
+  const int hv = virtual_heads(Hq, Hkv, Nq);
   int w = num_splits > 0 ? num_splits : default_workers();
   if (w > kMaxWorkers) w = kMaxWorkers;
-  const int per_head = w / Hkv > 0 ? w / Hkv : 1;
-  return per_head * Hkv;
+  const int per_head = w / hv > 0 ? w / hv : 1;
+  return per_head * hv;
 }
 
 int check_decode_shape(int dtype, int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
@@ -73,11 +83,14 @@ struct WorkspaceLayout {
   size_t part_lse_off, prefix_off, total;
 };
 
-// [pieces * M * d f32 partial O][pieces * M f32 partial LSE][(B+1) int64 prefix],
-// pieces = workers + B*Hkv (workers a multiple of Hkv); each part 256-byte aligned
+// [pieces * MP * d f32 partial O][pieces * MP f32 partial LSE][(B+1) int64 prefix],
+// MP = min(G*Nq, 16) rows per piece, pieces = workers + B*HV with HV the
+// (K/V head, row group) pairs and workers a multiple of HV; each part
+// 256-byte aligned
 WorkspaceLayout workspace_layout(int B, int Hq, int Hkv, int Nq, int d, int workers) {
-  const long long M = (long long)(Hq / Hkv) * Nq;
-  const long long pieces = (long long)workers + (long long)B * Hkv;
+  const long long rows = decode_rows(Hq, Hkv, Nq);
+  const long long M = rows < 16 ? rows : 16;
+  const long long pieces = (long long)workers + (long long)B * virtual_heads(Hq, Hkv, Nq);
   auto up = [](long long x) { return (x + 255) / 256 * 256; };
   WorkspaceLayout l;
   const long long o_bytes = up(pieces * M * d * 4);
@@ -128,14 +141,14 @@ int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_le
                            int num_splits) {
   const int st = check_decode_shape(ATTN_BF16, B, Hq, Hkv, Nq, d, max_seq_len, num_splits);
   if (st != ATTN_OK) return st;
-  return plan_workers(num_splits, Hkv);
+  return plan_workers(num_splits, Hq, Hkv, Nq);
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
                                    int num_splits) {
   if (check_decode_shape(ATTN_BF16, B, Hq, Hkv, Nq, d, max_seq_len, num_splits) != ATTN_OK)
     return 0;
-  return workspace_layout(B, Hq, Hkv, Nq, d, plan_workers(num_splits, Hkv)).total;
+  return workspace_layout(B, Hq, Hkv, Nq, d, plan_workers(num_splits, Hq, Hkv, Nq)).total;
 }
 
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -155,7 +168,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
       (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
       (reinterpret_cast<uintptr_t>(block_table) & 3u))
     return ATTN_EINVAL;
-  const int workers = plan_workers(num_splits, Hkv);
+  const int workers = plan_workers(num_splits, Hq, Hkv, Nq);
   const WorkspaceLayout lay = workspace_layout(B, Hq, Hkv, Nq, d, workers);
   if (workspace == nullptr || misaligned16(workspace) || workspace_bytes_given < lay.total)
     return ATTN_EWORKSPACE;

@@ -22,10 +22,13 @@
 //     wave j in sequence b lives at index kvh*(Wh + B) + j + b, which is
 //     unique. With fewer steps than waves only the first (number of steps)
 //     waves of a head run.
-//   * All G·Nq query rows that share the K/V head (G = Hq/Hkv query heads ×
-//     Nq new tokens, at most 16) are the 16 columns of
-//     v_mfma_f32_16x16x32_bf16, so every K/V byte is loaded once and used by
-//     all of them.
+//   * The G·Nq query rows that share a K/V head (G = Hq/Hkv query heads ×
+//     Nq new tokens, up to 64) are cut into groups of 16, each group the 16
+//     columns of v_mfma_f32_16x16x32_bf16: a K/V byte is loaded once per
+//     group and used by all of its rows. With G·Nq <= 16 (the usual decode
+//     shapes) there is one group, so every K/V byte is loaded once; the
+//     groups of one head run on neighbouring waves, so further groups
+//     mostly hit in L2.
 //   * Sᵀ = K·Qᵀ: K rows come straight from global memory into the A operand
 //     (lane = key, 8 consecutive d per lane), Qᵀ sits in registers.
 //   * Oᵀ = Vᵀ·Pᵀ: V rows are loaded 16 bytes per lane (8 consecutive d of one
@@ -37,9 +40,9 @@
 //     pool read as zeros (and are masked), so stale or NaN cache contents
 //     cannot leak into the result and no load needs a branch.
 //   * Partial results (normalised O and base-2 LSE per piece and row) go to
-//     the caller's workspace; the combine kernel merges the pieces of each
-//     segment in wave order with weights exp2(LSE_s - max LSE_s) and writes O
-//     (bf16) and the natural-log LSE.
+//     the caller's workspace; the combine kernel (one wave per output row)
+//     merges the pieces of each row in wave order with weights
+//     exp2(LSE_s - max LSE_s) and writes O (bf16) and the natural-log LSE.
 #include "common.h"
 #include "launch.h"
 
@@ -54,11 +57,14 @@ struct DecodeParams {
   const int32_t* seq_lens;
   __bf16* o;
   float* lse;
-  float* part_o;          // [Hkv * (Wh + B) pieces][M][D]
-  float* part_lse;        // [Hkv * (Wh + B) pieces][M]
+  float* part_o;          // [HV * (Wh + B) pieces][MP][D]
+  float* part_lse;        // [HV * (Wh + B) pieces][MP]
   long long* prefix;      // [B + 1]: 32-key steps of sequences 0..b-1
   int B, Hq, Hkv, Nq, G, M;
-  int W;                  // waves launched: Wh per K/V head
+  int RG;                 // groups of up to 16 query rows per K/V head
+  int MP;                 // rows per group (min(M, 16))
+  int HV;                 // (K/V head, row group) pairs: Hkv * RG
+  int W;                  // waves launched: Wh per (K/V head, row group)
   int Wh;
   float c;  // scale * log2(e)
   int causal;
@@ -128,11 +134,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (w >= p.W) return;
 
   // ---- this wave's range of 32-key steps --------------------------------------
-  // Wave w serves K/V head w % Hkv; the Wh waves of a head split that head's
-  // steps of all sequences laid end to end. Neighbouring waves thus read the
-  // same token rows of different heads.
-  const int kvh = w % p.Hkv;
-  const int j = w / p.Hkv;
+  // Wave w serves row group rg of K/V head kvh, vh = w % HV = kvh*RG + rg;
+  // the Wh waves of a (head, row group) split its steps of all sequences
+  // laid end to end. Neighbouring waves thus read the same token rows of
+  // the same or neighbouring heads.
+  const int vh = w % p.HV;
+  const int kvh = vh / p.RG;
+  const int rg = vh - kvh * p.RG;
+  const int j = w / p.HV;
   // Total steps per head; wave 0 also records the per-sequence prefix for the combine.
   long long tot = 0;
   for (int b0 = 0; b0 < p.B; b0 += 64) {
@@ -176,15 +185,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // loop-invariant lane byte offsets inside a 16-token stretch
   const int koff = r16 * rowb + 16 * g;         // K: token r16, d = 8*g (+32c via imm)
   const int voff = (4 * g) * rowb + 16 * r16;   // V: token 4*g (+jj via soffset), chunk r16
-  const bool row_ok = r16 < p.M;                // rows r = qi * G + h, r < M
-  const int qi = row_ok ? r16 / p.G : 0;
-  const int hrow = row_ok ? r16 % p.G : 0;
+  const int row = 16 * rg + r16;                // rows r = qi * G + h, r < M
+  const bool row_ok = r16 < p.MP && row < p.M;
+  const int qi = row_ok ? row / p.G : 0;
+  const int hrow = row_ok ? row % p.G : 0;
 
   // ---- one piece: keys [kb0, ke) of head kvh of sequence b ---------------------
   auto piece = [&](int b, int kvh, int n, int kb0, int ke, long long id)
       __attribute__((always_inline)) {
-    float* po = p.part_o + id * p.M * D;
-    float* pl = p.part_lse + id * p.M;
+    float* po = p.part_o + id * p.MP * D;
+    float* pl = p.part_lse + id * p.MP;
     int limit = ke;  // keys of this piece visible to the row: [kb0, limit)
     if (p.causal) limit = min(limit, n - p.Nq + qi + 1);
 
@@ -371,7 +381,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int lo = (int)(x - seg);
     const int hi = (int)min((long long)st_b, x1 - seg);
     const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
-    piece(b, kvh, n, 32 * lo, min(n, 32 * hi), (long long)kvh * (p.Wh + p.B) + j + b);
+    piece(b, kvh, n, 32 * lo, min(n, 32 * hi), (long long)vh * (p.Wh + p.B) + j + b);
     x = seg + hi;
     seg += st_b;
     do {
@@ -381,90 +391,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// One workgroup of 4 waves per (sequence, K/V head, query row). The pieces of
-// sequence b for head kvh were written by that head's waves w_first..w_last
-// at index kvh*(Wh + B) + b + j; wave i of the workgroup merges the pieces
-// w_first + i, + 4, ... with weights exp2(LSE - max LSE), and the four
-// partial sums are added in a fixed order through LDS, so the result is
-// deterministic. Each lane owns D/64 consecutive output elements.
+// One wave per (sequence, K/V head, query row), four rows per workgroup.
+// The pieces of sequence b for row r were written by waves w_first..w_last
+// of the row's (K/V head, row group) vh at index vh*(Wh + B) + b + j. The
+// wave's four 16-lane groups take every fourth piece (group q: pieces q,
+// q+4, ...), weight them by exp2(LSE - max LSE), and the group sums are then
+// added in a fixed order with lane exchanges, so the result is
+// deterministic. A lane owns D/16 consecutive output elements.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
-  constexpr int E = D / 64;  // elements per lane
-  __shared__ float red_acc[4][D];
-  __shared__ float red_tot[4];
-  const int wave = threadIdx.x >> 6;
+  constexpr int E = D / 16;  // elements per lane
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x % p.M;
-  const int bk = blockIdx.x / p.M;
-  const int b = bk / p.Hkv;
-  const int kvh = bk % p.Hkv;
+  const int grp = lane >> 4;
+  const int l16 = lane & 15;
+  const long long rid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rid >= (long long)p.B * p.Hkv * p.M) return;
+  const int r = (int)(rid % p.M);
+  const long long bk = rid / p.M;
+  const int b = (int)(bk / p.Hkv);
+  const int kvh = (int)(bk % p.Hkv);
   const int qi = r / p.G;
   const int hq = kvh * p.G + r % p.G;
-  const long long T = p.prefix[p.B];  // steps per head
-  const int We = (int)min((long long)p.Wh, T);  // waves per head that took a range
+  const long long T = p.prefix[p.B];  // steps per (head, row group)
+  const int We = (int)min((long long)p.Wh, T);  // waves per (head, row group) that took a range
   const int st_b = seq_steps(p, b);
   int w_first = 0, w_last = -1;
   if (st_b > 0) {
     w_first = wave_of(p.prefix[b], T, We);
     w_last = wave_of(p.prefix[b] + st_b - 1, T, We);
   }
-  const long long first = (long long)kvh * (p.Wh + p.B) + b + w_first;
-  const float* pl = p.part_lse + first * p.M + r;
-  const float* po = p.part_o + (first * p.M + r) * D + E * lane;
+  const int vh = kvh * p.RG + r / 16;  // row r lives in row group r / 16, slot r % 16
+  const long long first = (long long)vh * (p.Wh + p.B) + b + w_first;
+  const float* pl = p.part_lse + first * p.MP + (r % 16);
+  const float* po = p.part_o + (first * p.MP + (r % 16)) * D + E * l16;
+  const long long so = (long long)p.MP * D;  // stride between pieces in part_o
   const int used = w_last - w_first + 1;
 
   float mx = neg_inf();
-  for (int i = 0; i < used; ++i)
-    mx = __builtin_elementwise_maximum(mx, pl[(long long)i * p.M]);
-  float acc[E];
+  for (int i = grp; i < used; i += 4)
+    mx = __builtin_elementwise_maximum(mx, pl[(long long)i * p.MP]);
+  mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16, 64));
+  mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32, 64));
+  f32x4_t acc[E / 4];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int e = 0; e < E / 4; ++e) acc[e] = f32x4_t{};
   float tot = 0.f;
   if (mx != neg_inf()) {
-    int i = wave;
-    for (; i + 12 < used; i += 16) {  // four pieces in flight per lane
-      float wt[4];
-      float v[4][E];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float ls = pl[(long long)(i + 4 * u) * p.M];
-        wt[u] = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[u][e] = po[(long long)(i + 4 * u) * p.M * D + e];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        tot += wt[u];
-#pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wt[u], v[u][e], acc[e]);
-      }
-    }
-    for (; i < used; i += 4) {
-      const float ls = pl[(long long)i * p.M];
+    for (int i = grp; i < used; i += 4) {
+      const float ls = pl[(long long)i * p.MP];
       const float wt = (ls == neg_inf()) ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
       tot += wt;
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(po + (long long)i * so);
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        acc[e] = __builtin_fmaf(wt, po[(long long)i * p.M * D + e], acc[e]);
+      for (int e = 0; e < E / 4; ++e) acc[e] += wt * src[e];
     }
   }
+  // add the four groups' sums: (g0 + g1) + (g2 + g3) in every lane
 #pragma unroll
-  for (int e = 0; e < E; ++e) red_acc[wave][E * lane + e] = acc[e];
-  if (lane == 0) red_tot[wave] = tot;
-  __syncthreads();
-  if (wave == 0) {
-    const float t = (red_tot[0] + red_tot[1]) + (red_tot[2] + red_tot[3]);
-    const float inv = t > 0.f ? 1.f / t : 0.f;
-    __bf16* op = p.o + (((long long)b * p.Nq + qi) * p.Hq + hq) * D + E * lane;
+  for (int sh = 16; sh <= 32; sh <<= 1) {
+    tot += __shfl_xor(tot, sh, 64);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int d = E * lane + e;
-      const float a = (red_acc[0][d] + red_acc[1][d]) + (red_acc[2][d] + red_acc[3][d]);
-      op[e] = (__bf16)(a * inv);
-    }
-    if (lane == 0 && p.lse != nullptr)
+    for (int e = 0; e < E / 4; ++e)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[e][c] += __shfl_xor(acc[e][c], sh, 64);
+  }
+  if (grp == 0) {
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    __bf16* op = p.o + (((long long)b * p.Nq + qi) * p.Hq + hq) * D + E * l16;
+#pragma unroll
+    for (int e = 0; e < E / 4; ++e)
+      *reinterpret_cast<bf16x4_t*>(op + 4 * e) = __builtin_convertvector(acc[e] * inv, bf16x4_t);
+    if (l16 == 0 && p.lse != nullptr)
       p.lse[((long long)b * p.Hq + hq) * p.Nq + qi] =
-          t > 0.f ? (mx + __builtin_amdgcn_logf(t)) * kLn2 : neg_inf();
+          tot > 0.f ? (mx + __builtin_amdgcn_logf(tot)) * kLn2 : neg_inf();
   }
 }
 
@@ -493,13 +492,17 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   pp.Nq = a.Nq;
   pp.G = a.Hq / a.Hkv;
   pp.M = pp.G * a.Nq;
-  pp.Wh = a.workers / a.Hkv;
-  pp.W = pp.Wh * a.Hkv;
+  if (pp.M <= 0) return hipSuccess;  // no query rows
+  pp.RG = (pp.M + 15) / 16;
+  pp.MP = pp.M < 16 ? pp.M : 16;
+  pp.HV = a.Hkv * pp.RG;
+  pp.Wh = a.workers / pp.HV;
+  pp.W = pp.Wh * pp.HV;
   pp.c = a.scale * kLog2e;
   pp.causal = a.causal;
   if (a.B <= 0 || pp.Wh <= 0) return hipSuccess;
   const long long blocks = (pp.W + 3) / 4;
-  const long long cblocks = (long long)a.B * a.Hkv * pp.M;
+  const long long cblocks = ((long long)a.B * a.Hkv * pp.M + 3) / 4;
   if (blocks > 0x7fffffffLL || cblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.d == 128) {
     hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((int)blocks), dim3(256), 0, s, pp);

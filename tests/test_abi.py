@@ -100,7 +100,7 @@ def _decode(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=0), eta.ATTN_EUNSUPPORTED),       # fp32 decode not built
-    (dict(Nq=5), eta.ATTN_EUNSUPPORTED),          # 4 heads x 5 rows > 16
+    (dict(Nq=17), eta.ATTN_EUNSUPPORTED),         # 4 heads x 17 rows > 64
     (dict(d=80), eta.ATTN_EUNSUPPORTED),
     (dict(Hq=30), eta.ATTN_EINVAL),
     (dict(L=-1), eta.ATTN_EINVAL),
@@ -125,14 +125,22 @@ def test_worker_plan_and_workspace_size():
     assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 100, 3) == 8
     assert lib.attn_decode_num_splits(1, 32, 8, 1, 128, 100, 20) == 16
     assert lib.attn_decode_num_splits(1, 32, 2, 1, 128, 100, 7) == 6
-    assert lib.attn_decode_num_splits(1, 32, 8, 5, 128, 1000, 0) == eta.ATTN_EUNSUPPORTED
+    # more than 16 rows per K/V head: groups of 16 rows, workers a multiple of Hkv * groups
+    assert lib.attn_decode_num_splits(1, 32, 4, 4, 128, 100, 20) == 16   # G*Nq = 32: 2 groups
+    assert lib.attn_decode_num_splits(1, 16, 1, 4, 128, 100, 7) == 4     # G*Nq = 64: 4 groups
+    assert lib.attn_decode_num_splits(1, 32, 8, 16, 128, 1000, 0) > 0     # G*Nq = 64
+    assert lib.attn_decode_num_splits(1, 32, 8, 17, 128, 1000, 0) == eta.ATTN_EUNSUPPORTED
     # pieces = workers + B*Hkv; [pieces*M*d f32][pieces*M f32][(B+1) int64], 256-byte aligned
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
     pieces = 96 + 16 * 8  # 100 requested -> 12 per K/V head
     M = 4
     want = up(pieces * M * 128 * 4) + up(pieces * M * 4) + 17 * 8
     assert lib.attn_decode_workspace_bytes(16, 32, 8, 1, 128, 32768, 100) == want
-    assert lib.attn_decode_workspace_bytes(16, 32, 8, 9, 128, 32768, 0) == 0
+    assert lib.attn_decode_workspace_bytes(16, 32, 8, 17, 128, 32768, 0) == 0
+    # G*Nq = 32 rows: pieces of 16 rows, virtual heads = Hkv * 2
+    pieces = 96 + 16 * 16
+    want = up(pieces * 16 * 128 * 4) + up(pieces * 16 * 4) + 17 * 8
+    assert lib.attn_decode_workspace_bytes(16, 32, 8, 8, 128, 32768, 100) == want
 
 
 def test_kv_append_and_gather_reject():

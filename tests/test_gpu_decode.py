@@ -1,6 +1,7 @@
 """GPU parity of kv_append + attn_decode_paged against the fp64 oracle.
 
-Covers contiguous and paged caches, Nq in {1, 2, 4, 8}, group sizes 1..16,
+Covers contiguous and paged caches, Nq in {1, 2, 4, 5, 8, 64}, group sizes 1..16
+(G*Nq up to 64 rows, in groups of 16),
 head dims 64/128, causal and not, explicit and default split counts, ragged
 lengths, rows that see no key, invalid table entries, NaN-poisoned unused
 cache rows, bitwise determinism and output guard bands; plus the split-KV
@@ -34,6 +35,12 @@ def _dev(inp, dev):
     (2, 16, 1, 1, 128, 16, 16, True, 0),     # G=16, block-aligned lengths
     (2, 8, 4, 2, 64, 1, 40, True, 50),       # more splits than 32-key steps
     (1, 4, 2, 4, 128, 3000, 3000, True, 7),
+    # more than 16 rows per K/V head: groups of 16 rows
+    (2, 32, 4, 4, 128, 100, 700, True, 0),    # G=8, Nq=4: 32 rows, 2 groups
+    (2, 16, 1, 4, 64, 40, 300, True, 5),      # G=16, Nq=4: 64 rows, 4 groups
+    (3, 8, 2, 5, 128, 5, 200, True, 0),       # G=4, Nq=5: 20 rows, ragged second group
+    (2, 2, 2, 64, 128, 64, 400, True, 0),     # G=1, Nq=64: 64 query tokens, causal offsets
+    (2, 32, 8, 8, 128, 50, 500, False, 3),    # G=4, Nq=8: 32 rows, not causal
 ])
 def test_paged_small(B, Hq, Hkv, Nq, d, lo, hi, causal, splits):
     dev = need_gpu()
