@@ -117,7 +117,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
  *                 of per-sequence step counts, all written before they are
  *                 read, so it needs no clearing. Calls that share one
  *                 workspace must be ordered on one stream.
- * Supported: dtype ATTN_BF16, d in {64, 128}, (Hq/Hkv)·Nq <= 16.
+ * Supported: dtype ATTN_BF16, d in {64, 128}, (Hq/Hkv)·Nq <= 64.
  */
 int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
