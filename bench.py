@@ -10,8 +10,9 @@ seeded workload with inputs already resident in HBM:
     cached lengths uniform in [1024, 16384],
   * split-KV decode of 1 token against 16 contiguous 32768-token caches.
 Each stage is timed with HIP events recorded on the stream the library
-launches on; the long-context prefill (N=32768) and the fp32 single-head case
-are timed in their own loops after the steps. FLOPs count visible
+launches on; the long-context prefill (N=32768), the chunked prefill against
+the paged cache (8 sequences, 512 new tokens after 1k-8k cached ones) and the
+fp32 single-head case are timed in their own loops after the steps. FLOPs count visible
 (query, key) pairs x 4d; decode bytes count each visible K/V row once.
 Prints ONE JSON line.
 """
@@ -47,6 +48,11 @@ def prefill_flops(B, Hq, N, d, causal=True):
     return 4.0 * d * B * Hq * pairs
 
 
+def chunk_flops(seq_lens, Nq, Hq, d):
+    """Causal chunk of Nq new rows after seq_len - Nq cached keys, per sequence."""
+    return 4.0 * d * Hq * sum(causal_pairs(Nq, n, n - Nq) for n in seq_lens)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -56,7 +62,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", default=None,
                     choices=["prefill_4k", "prefill_32k", "splitkv_decode_32k", "paged_decode_q4",
-                             "copy_1gib"],
+                             "chunked_prefill_paged", "copy_1gib"],
                     help="run only this stage --steps times and exit (for profiler runs); "
                          "copy_1gib is a plain 1 GiB device copy used to calibrate HBM counters")
     return ap.parse_args()
@@ -75,6 +81,12 @@ def run_stage(args, torch, eta, inputs, dev):
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         fn = lambda: eta.attn_prefill(q, k, v, causal=True, out=o, lse=lse)  # noqa: E731
+    elif name == "chunked_prefill_paged":
+        p = inputs.workload_inputs(name, dev)
+        eta.kv_append(p["k_new"], p["v_new"], p["k_pool"], p["v_pool"], p["cache_lens"],
+                      block_table=p["block_table"])
+        fn = lambda: eta.attn_prefill_paged(p["q"], p["k_pool"], p["v_pool"], p["seq_lens"],  # noqa
+                                            block_table=p["block_table"], causal=True)
     elif name == "splitkv_decode_32k":
         q, kc, vc, sl = inputs.workload_inputs(name, dev)
         fn = lambda: eta.attn_decode_paged(q, kc, vc, sl, causal=True)  # noqa: E731
@@ -303,6 +315,34 @@ def main():
         "ms": round(ms3, 4), "TFLOP/s": round(flops3 / (ms3 * 1e-3) / 1e12, 2),
         "frac_of_peak": round(flops3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops": flops3}
+    del q3, k3, v3, o3, l3
+    torch.cuda.empty_cache()
+    # chunked prefill against the paged cache: 512 new tokens per sequence
+    w6 = inputs.WORKLOADS["chunked_prefill_paged"]
+    p6 = inputs.workload_inputs("chunked_prefill_paged", dev)
+    eta.kv_append(p6["k_new"], p6["v_new"], p6["k_pool"], p6["v_pool"], p6["cache_lens"],
+                  block_table=p6["block_table"])
+    o6 = torch.empty_like(p6["q"])
+    l6 = torch.empty((w6["B"], w6["Hq"], w6["Nq"]), dtype=torch.float32, device=dev)
+
+    def chunk6():
+        eta.attn_prefill_paged(p6["q"], p6["k_pool"], p6["v_pool"], p6["seq_lens"],
+                               block_table=p6["block_table"], causal=True, out=o6, lse=l6)
+
+    t6 = StageTimer(torch, stream, ["p"])
+    for _ in range(3):
+        chunk6()
+    for _ in range(20):
+        t6.run("p", chunk6)
+    torch.cuda.synchronize()
+    ms6 = t6.mean_ms("p")
+    flops6 = chunk_flops([int(x) for x in p6["seq_lens"].cpu()], w6["Nq"], w6["Hq"], w6["d"])
+    result_workloads["chunked_prefill_paged"] = {
+        "ms": round(ms6, 5), "TFLOP/s": round(flops6 / (ms6 * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(flops6 / (ms6 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flops": flops6}
+    del p6, o6, l6
+    torch.cuda.empty_cache()
     q1, k1, v1 = inputs.workload_inputs("single_head_f32", dev)
     t1 = StageTimer(torch, stream, ["p"])
     for _ in range(10):

@@ -54,6 +54,8 @@ def _load():
     P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_prefill.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill.restype = I
+    lib.attn_prefill_paged.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I, I, P]
+    lib.attn_prefill_paged.restype = I
     lib.attn_decode_paged.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I, I, I,
                                       P, SZ, P]
     lib.attn_decode_paged.restype = I
@@ -129,6 +131,49 @@ def attn_prefill(q, k, v, scale=None, causal=False, q_offset=0, out=None, lse=No
                           Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(q_offset),
                           _stream(q.device))
     _check(st, "attn_prefill")
+    return out, lse
+
+
+def _check_cache_args(q, k_cache, v_cache, seq_lens, block_table):
+    B, Nq, Hq, d = q.shape
+    if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must share a shape with head dim d")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B, max_blocks]")
+        if k_cache.shape[1] != BLOCK_TOKENS:
+            raise ValueError("a paged cache is [num_blocks, 16, Hkv, d]")
+    elif k_cache.shape[0] != B:
+        raise ValueError("a contiguous cache is [B, max_len, Hkv, d]")
+
+
+def attn_prefill_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=None, causal=True,
+                       max_seq_len=None, out=None, lse=None, want_lse=True):
+    """Chunked prefill against a cache. q [B,Nq,Hq,d]; caches [P,16,Hkv,d] (paged) or
+    [B,L,Hkv,d] (contiguous); seq_lens [B] int32 (keys incl. the Nq new ones)
+    -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
+    lib = _load()
+    _need_gpu(q, k_cache, v_cache, seq_lens, block_table)
+    _check_cache_args(q, k_cache, v_cache, seq_lens, block_table)
+    B, Nq, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _need_gpu(out, lse)
+    st = lib.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), mb,
+                                nblocks, _ptr(seq_lens), _ptr(out), _ptr(lse), _dtype_code(q), B,
+                                Hq, Hkv, Nq, d, float(scale), int(bool(causal)), L,
+                                _stream(q.device))
+    _check(st, "attn_prefill_paged")
     return out, lse
 
 
@@ -227,6 +272,7 @@ def attn_gather_paged(cache, seq_lens, block_table=None, max_seq_len=None, out=N
 
 __all__ = [
     "attn_prefill",
+    "attn_prefill_paged",
     "attn_decode_paged",
     "attn_decode_num_splits",
     "attn_decode_workspace_bytes",

@@ -125,6 +125,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   if (q_offset > (1 << 30) || q_offset < -(1 << 30)) return ATTN_EINVAL;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
   if (!head_dim_ok(d)) return ATTN_EUNSUPPORTED;
+  // one K/V head's rows are addressed with 32-bit byte offsets
+  if ((long long)Nk * d * 4 > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (q == nullptr || o == nullptr) return ATTN_EINVAL;
   if (Nk > 0 && (k == nullptr || v == nullptr)) return ATTN_EINVAL;
@@ -135,6 +137,37 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, s)
                                       : attn::launch_prefill_f32(a, s));
+}
+
+int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                       const int32_t* seq_lens, void* o, float* lse, int dtype, int B, int Hq,
+                       int Hkv, int Nq, int d, float scale, int causal, int max_seq_len,
+                       void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || max_seq_len < 0) return ATTN_EINVAL;
+  if (Hq % Hkv != 0) return ATTN_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  if (block_table != nullptr && (max_blocks_per_seq <= 0 || num_blocks < 0)) return ATTN_EINVAL;
+  if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (!head_dim_ok(d)) return ATTN_EUNSUPPORTED;
+  // one 16-token block of a head is addressed with 32-bit byte offsets
+  if ((long long)16 * Hkv * d * 2 > 0x7fffffffLL) return ATTN_EUNSUPPORTED;
+  if (B == 0 || Nq == 0) return ATTN_OK;
+  if (q == nullptr || o == nullptr || seq_lens == nullptr) return ATTN_EINVAL;
+  if (max_seq_len > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_EINVAL;
+  if (misaligned16(q) || misaligned16(o) || misaligned16(k_cache) || misaligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return ATTN_EINVAL;
+  attn::PrefillArgs a{q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, 0, d, scale, causal != 0, 0};
+  a.q_token_major = 1;
+  a.cache = 1;
+  a.block_table = block_table;
+  a.max_blocks = block_table ? max_blocks_per_seq : 0;
+  a.num_blocks = block_table ? num_blocks : 0;
+  a.max_len = max_seq_len;
+  a.seq_lens = seq_lens;
+  return status_of(attn::launch_prefill_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,

@@ -19,6 +19,14 @@ struct PrefillArgs {
   float scale;
   int causal;
   int q_offset;
+  int q_token_major = 0;  // q, o are [B, Nq, Hq, d] (else [B, Hq, Nq, d])
+  // cache != 0: k, v are a token-major cache, [num_blocks, 16, Hkv, d] pools
+  // behind block_table or [B, max_len, Hkv, d] when block_table is null;
+  // Nk and q_offset then come from seq_lens per sequence
+  int cache = 0;
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, num_blocks = 0, max_len = 0;
+  const int32_t* seq_lens = nullptr;
 };
 
 struct DecodeArgs {

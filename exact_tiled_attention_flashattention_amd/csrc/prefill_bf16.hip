@@ -33,9 +33,6 @@
 #include "common.h"
 #include "launch.h"
 
-#ifndef ATTN_PREFILL_SCHED
-#define ATTN_PREFILL_SCHED 0
-#endif
 
 namespace attn {
 namespace {
@@ -59,6 +56,14 @@ struct PrefillParams {
   int n_hgrp;  // workgroups per K/V head and query block (G / hw)
   float c;     // scale * log2(e)
   int q_offset;
+  long long sqb, sqh, sqr;  // element strides of q and o: batch, head, row
+  // token-major K/V cache (CACHE kernels): k, v are [num_blocks, 16, Hkv, D]
+  // pools behind `table`, or [B, max_len, Hkv, D] when `table` is null;
+  // sequence b has clamp(seq_lens[b]) keys and its query row i sits at
+  // position seq_lens[b] - Nq + i
+  const int32_t* table;
+  int max_blocks, num_blocks, max_len;
+  const int32_t* seq_lens;
 };
 
 // K/V tiles live in LDS unpadded (D*2 bytes per key row) with the 16-byte
@@ -78,7 +83,7 @@ __device__ __forceinline__ int lds_off(int row, int elem) {  // byte offset of e
   return row * (D * 2) + ((((elem >> 3) ^ swz<D>(row))) << 4) + ((elem & 7) << 1);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool CACHE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillParams p) {
   constexpr int NDC = D / 16;              // k-steps of the Q·Kᵀ contraction
@@ -101,14 +106,44 @@ void prefill_bf16_kernel(PrefillParams p) {
   const int g = lane >> 5;
 
   // ---- which rows this workgroup and wave own --------------------------------
-  const int per_q = p.B * p.Hkv * p.n_hgrp;
-  const int qrank = blockIdx.x / per_q;
-  int rest = blockIdx.x - qrank * per_q;
-  const int qblk = CAUSAL ? (p.n_qblk - 1 - qrank) : qrank;  // longest first
-  const int hg = rest % p.n_hgrp;
-  rest /= p.n_hgrp;
-  const int kvh = rest % p.Hkv;
-  const int b = rest / p.Hkv;
+  // Workgroups are launched longest first. Slabs: by query block (causal
+  // blocks near the end see the most keys). Cache: by sequence, the longest
+  // first (a sequence's cached length dominates its work), then by query
+  // block.
+  int qrank, hg, kvh, b;
+  if constexpr (!CACHE) {
+    const int per_q = p.B * p.Hkv * p.n_hgrp;
+    qrank = blockIdx.x / per_q;
+    int rest = blockIdx.x - qrank * per_q;
+    hg = rest % p.n_hgrp;
+    rest /= p.n_hgrp;
+    kvh = rest % p.Hkv;
+    b = rest / p.Hkv;
+  } else {
+    const int per_s = p.Hkv * p.n_hgrp;
+    const int per_b = p.n_qblk * per_s;
+    const int slot = blockIdx.x / per_b;
+    int rest = blockIdx.x - slot * per_b;
+    qrank = rest / per_s;
+    rest -= qrank * per_s;
+    hg = rest % p.n_hgrp;
+    kvh = rest / p.n_hgrp;
+    b = slot;
+    if (p.B <= 64) {
+      // the sequence of rank `slot` when ordered by length (longest first,
+      // ties by index): lane l ranks sequence l against all others
+      const int n_l = lane < p.B ? p.seq_lens[lane] : 0;
+      int rank = 0;
+      for (int j = 0; j < p.B; ++j) {
+        const int n_j = __builtin_amdgcn_readlane(n_l, j);
+        rank += (n_j > n_l || (n_j == n_l && j < lane)) ? 1 : 0;
+      }
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < p.B && rank == slot);
+      b = hit != 0 ? __builtin_ctzll(hit) : slot;
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+  }
+  const int qblk = CAUSAL ? (p.n_qblk - 1 - qrank) : qrank;
 
   const int head_local = wave % p.hw;
   const int sub = wave / p.hw;
@@ -116,28 +151,40 @@ void prefill_bf16_kernel(PrefillParams p) {
   const int q0 = qblk * 32 * p.pw;
   const int my_q = q0 + sub * 32 + l32;
 
-  int kend = p.Nk;
+  // keys of this sequence and the position of query row 0
+  int nk = p.Nk;
+  int qoff = p.q_offset;
+  if constexpr (CACHE) {
+    long long cap = p.max_len;
+    if (p.table != nullptr && (long long)p.max_blocks * kBlockTokens < cap)
+      cap = (long long)p.max_blocks * kBlockTokens;
+    const int n = p.seq_lens[b];
+    nk = n < 0 ? 0 : (n > cap ? (int)cap : n);
+    qoff = nk - p.Nq;
+  }
+
+  int kend = nk;
   if (CAUSAL) {
     const int last_row = min(q0 + 32 * p.pw, p.Nq) - 1;
-    const long long lim = (long long)last_row + p.q_offset + 1;
+    const long long lim = (long long)last_row + qoff + 1;
     if (lim < kend) kend = (int)(lim < 0 ? 0 : lim);
   }
   const int ntiles = (kend + kBN - 1) / kBN;
-  long long mask_from = p.Nk;  // first key some row of the workgroup cannot see
+  long long mask_from = nk;  // first key some row of the workgroup cannot see
   if (CAUSAL) {
-    const long long first = (long long)q0 + p.q_offset + 1;
+    const long long first = (long long)q0 + qoff + 1;
     if (first < mask_from) mask_from = first;
   }
   // this lane's last visible key (clamped into int range)
-  long long lim64 = CAUSAL ? (long long)my_q + p.q_offset : (long long)p.Nk - 1;
-  if (lim64 > (long long)p.Nk - 1) lim64 = (long long)p.Nk - 1;
+  long long lim64 = CAUSAL ? (long long)my_q + qoff : (long long)nk - 1;
+  if (lim64 > (long long)nk - 1) lim64 = (long long)nk - 1;
   if (lim64 < -1) lim64 = -1;
   const int lim = (int)lim64;
 
   // ---- Qᵀ as the B operand: lane holds row my_q, d = 16*dc + 8*g + j ---------
   bf16x8_t qf[NDC];
   {
-    const __bf16* qp = p.q + (((long long)b * p.Hq + hq) * p.Nq + my_q) * D + 8 * g;
+    const __bf16* qp = p.q + b * p.sqb + hq * p.sqh + my_q * p.sqr + 8 * g;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
       if (my_q < p.Nq)
@@ -147,39 +194,106 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
   }
 
-  const long long kv_base = ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
-  const __bf16* kg = p.k + kv_base;
-  const __bf16* vg = p.v + kv_base;
-
-  // Direct global->LDS loads through buffer resources (one per K/V head, range
-  // Nk rows): instruction i of this wave fills LDS bytes
-  // [(wave*NI + i)*1024, +1024), lane l its 16 bytes at +16*l, i.e. physical
-  // chunk (lin % CPR) of row (lin / CPR); the lane fetches the logical chunk
-  // that the swizzle stores there. The per-lane byte offsets do not depend on
-  // the tile; rows at or past Nk fall outside the resource and arrive as zeros
-  // (those keys are masked).
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, p.Nk * D * 2, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, p.Nk * D * 2, kBufferFlags);
-  // Lane part of the byte offset: instruction i of the wave adds
-  // (wave*NI + i)*1024 (scalar) and flips the chunk bits that the swizzle
-  // takes from the row's instruction index (one XOR). For d = 128 a
+  // Direct global->LDS loads through buffer resources: instruction i of this
+  // wave fills LDS bytes [(wave*NI + i)*1024, +1024), lane l its 16 bytes at
+  // +16*l, i.e. physical chunk (lin % CPR) of tile row (lin / CPR); the lane
+  // fetches the logical chunk that the swizzle stores there. Rows outside a
+  // resource's range arrive as zeros (those keys are masked). For d = 128 a
   // 1 KiB instruction covers rows 4*(wave*NI+i) + lane/16, swz = 4*(lane/16) + i;
-  // for d = 64 rows 8*(wave*NI+i) + lane/8, swz = 4*i + lane/16.
-  const int lane_base = (D == 128)
-      ? ((lane >> 4) * 256) | (16 * ((lane & 15) ^ (4 * (lane >> 4))))
-      : ((lane >> 3) * 128) | (16 * ((lane & 7) ^ (lane >> 4)));
+  // for d = 64 rows 8*(wave*NI+i) + lane/8, swz = 4*i + lane/16: the
+  // instruction index only flips chunk bits (one XOR).
   constexpr int kXorStep = (D == 128) ? 16 : 64;
-  auto issue = [&](__amdgpu_buffer_rsrc_t rs, int k0, char* dst) {
-    int lb = lane_base;
+  constexpr int RPI = 1024 / (D * 2);  // tile rows per load instruction
+  auto lane_offset = [&](int row_bytes) {
+    return (D == 128) ? ((lane >> 4) * row_bytes) | (16 * ((lane & 15) ^ (4 * (lane >> 4))))
+                      : ((lane >> 3) * row_bytes) | (16 * ((lane & 7) ^ (lane >> 4)));
+  };
+  auto load_rows = [&](__amdgpu_buffer_rsrc_t rs, int soff, int row_bytes, char* dst)
+      __attribute__((always_inline)) {
+    int lb = lane_offset(row_bytes);
     asm volatile("" : "+v"(lb));  // recompute the offsets here instead of keeping them live
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(dst + (wave * NI + i) * 1024),
                                                16, lb ^ (kXorStep * i),
-                                               k0 * D * 2 + (wave * NI + i) * 1024, 0, 0);
+                                               soff + i * RPI * row_bytes, 0, 0);
   };
+
+  // [B, Hkv, Nk, D] slabs: one resource per K/V head (range Nk rows); the
+  // tile's rows are contiguous, wave w's share starts at row 16w.
+  const long long kv_base = CACHE ? 0 : ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_base), 0, CACHE ? 0 : p.Nk * D * 2,
+                                        kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_base), 0, CACHE ? 0 : p.Nk * D * 2,
+                                        kBufferFlags);
+
+  // Token-major cache: a 64-key tile is four 16-token blocks and wave w loads
+  // block 4t + w of tile t (tile rows 16w..16w+15) through a resource that
+  // ends after the block's last valid row. The block table's entries for 64
+  // consecutive blocks sit one per lane in `tab` and are picked with readlane.
+  const int rowb = p.Hkv * D * 2;  // bytes between consecutive tokens of one head
+  int tab = -1;
+  int tab_base = -(1 << 30);
+  auto tab_window = [&](int t) {  // entries of blocks 4t-8 .. 4t+3 become readable
+    if (p.table != nullptr && 4 * t + 3 - tab_base >= 64) {
+      tab_base = max(0, 4 * t - 8);
+      const int i = tab_base + lane;
+      tab = i < p.max_blocks ? p.table[(long long)b * p.max_blocks + i] : -1;
+    }
+  };
+  // physical block of logical block jb, or -1 when the entry is invalid
+  auto block_of = [&](int jb) -> int {
+    if (p.table == nullptr) return jb;
+    const int e = __builtin_amdgcn_readlane(tab, jb - tab_base);
+    return (e >= 0 && e < p.num_blocks) ? e : -1;
+  };
+  auto load_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
+    const int jb = 4 * t + wave;
+    const int e = block_of(jb);
+    const int valid = min(kBlockTokens, nk - kBlockTokens * jb);
+    const bool ok = e >= 0 && valid > 0;
+    long long row0 = 0;  // element offset of slot 0 of the block, head kvh
+    if (ok)
+      row0 = p.table == nullptr
+                 ? ((long long)b * p.max_len + (long long)kBlockTokens * jb) * p.Hkv * D + kvh * D
+                 : ((long long)e * kBlockTokens * p.Hkv + kvh) * D;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(pool + row0), 0, ok ? (valid - 1) * rowb + D * 2 : 0, kBufferFlags);
+    load_rows(rs, 0, rowb, dst);
+  };
+  // bit q: block 4t + q of tile t has storage (blocks past the sequence count
+  // as present; their keys are masked by position)
+  auto tile_ok_bits = [&](int t) -> unsigned {
+    unsigned bits = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int jb = 4 * t + q;
+      const bool ok = nk - kBlockTokens * jb <= 0 || block_of(jb) >= 0;
+      bits |= (ok ? 1u : 0u) << q;
+    }
+    return bits;
+  };
+  // tile t's K, V into LDS; issue_k returns the tile's block bits (cache)
+  auto issue_k = [&](int t, char* dst) __attribute__((always_inline)) -> unsigned {
+    if constexpr (CACHE) {
+      tab_window(t);
+      load_block(p.k, t, dst);
+      return tile_ok_bits(t);
+    } else {
+      load_rows(krs, t * kBN * D * 2 + wave * NI * 1024, D * 2, dst);
+      return 0xFu;
+    }
+  };
+  auto issue_v = [&](int t, char* dst) __attribute__((always_inline)) {
+    if constexpr (CACHE)
+      load_block(p.v, t, dst);
+    else
+      load_rows(vrs, t * kBN * D * 2 + wave * NI * 1024, D * 2, dst);
+  };
+  // block bits of tiles it, it+1, it+2 in bits [3:0], [7:4], [11:8]
+  unsigned okq = 0xFFFu;
 
   // Sᵀ[key][row] of one tile: two 32-key halves, K (A operand) from LDS
   auto scores = [&](const char* kl, f32x16_t (&s)[2]) {
@@ -194,16 +308,21 @@ void prefill_bf16_kernel(PrefillParams p) {
       }
     }
   };
-  // only tiles past the first row's diagonal or the ragged end hide keys
-  auto needs_mask = [&](int k0) { return k0 + kBN > mask_from || k0 + kBN > p.Nk; };
-  // hide the keys a row cannot see
+  // only tiles past the first row's diagonal, the ragged end or a missing
+  // cache block hide keys
+  auto needs_mask = [&](int k0) {
+    return k0 + kBN > mask_from || k0 + kBN > nk || (CACHE && (okq & 0xFu) != 0xFu);
+  };
+  // hide the keys a row cannot see (key slot i of half kb lies in block
+  // 2*kb + (i >= 8) of the tile)
   auto mask = [&](int k0, f32x16_t (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key > lim) s[kb][i] = neg_inf();
+        const bool stored = !CACHE || ((okq >> (2 * kb + (i >= 8 ? 1 : 0))) & 1u);
+        if (key > lim || !stored) s[kb][i] = neg_inf();
       }
   };
 
@@ -251,8 +370,8 @@ void prefill_bf16_kernel(PrefillParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it+1) and V(it) have landed
     __syncthreads();                     // ... for every wave; the free buffers are free
     if (!LAST) {
-      if (it + 2 < ntiles) issue(krs, k0 + 2 * kBN, kfree);
-      issue(vrs, k0 + kBN, vfree);
+      if (it + 2 < ntiles) okq |= issue_k(it + 2, kfree) << 8;
+      issue_v(it + 1, vfree);
     }
     if (needs_mask(k0)) {
       mask(k0, sc);
@@ -292,19 +411,6 @@ void prefill_bf16_kernel(PrefillParams p) {
         pk[kb][j] = pack_bf16x2(e0, e1);
       }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-#if ATTN_PREFILL_SCHED
-    if (!LAST) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      }
-    }
-#endif
 
     // ---- phase 2: Oᵀ += Vᵀ Pᵀ, 16 keys per MFMA; Vᵀ via transposing LDS reads ----
 #pragma unroll
@@ -330,22 +436,13 @@ void prefill_bf16_kernel(PrefillParams p) {
         }
       }
     if (!LAST) mt = tile_max(sn);
-#if ATTN_PREFILL_SCHED
-#pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 1);
-    }
-#endif
+    okq >>= 4;
   };
 
   if (ntiles > 0) {
-    issue(krs, 0, kb0);
-    issue(vrs, 0, vb0);
-    if (ntiles > 1) issue(krs, kBN, kb1);
+    okq = issue_k(0, kb0);
+    issue_v(0, vb0);
+    if (ntiles > 1) okq |= issue_k(1, kb1) << 4;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     f32x16_t sa[2], sb[2];
@@ -372,7 +469,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   const float l_tot = sum_across_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (my_q < p.Nq) {
-    __bf16* op = p.o + (((long long)b * p.Hq + hq) * p.Nq + my_q) * D;
+    __bf16* op = p.o + b * p.sqb + hq * p.sqh + my_q * p.sqr;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -389,10 +486,20 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool CACHE>
 hipError_t launch_typed(const PrefillParams& pp, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3(nblocks), dim3(kWaves * 64), 0, s, pp);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, CACHE>), dim3(nblocks), dim3(kWaves * 64), 0,
+                     s, pp);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillParams& pp, bool causal, bool cache, int nblocks, hipStream_t s) {
+  if (cache)
+    return causal ? launch_typed<D, true, true>(pp, nblocks, s)
+                  : launch_typed<D, false, true>(pp, nblocks, s);
+  return causal ? launch_typed<D, true, false>(pp, nblocks, s)
+                : launch_typed<D, false, false>(pp, nblocks, s);
 }
 
 }  // namespace
@@ -416,14 +523,27 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   pp.n_hgrp = pp.G / pp.hw;
   pp.c = a.scale * kLog2e;
   pp.q_offset = a.q_offset;
+  const long long d = a.d;
+  if (a.q_token_major) {  // [B, Nq, Hq, d]
+    pp.sqr = (long long)a.Hq * d;
+    pp.sqh = d;
+    pp.sqb = (long long)a.Nq * a.Hq * d;
+  } else {  // [B, Hq, Nq, d]
+    pp.sqr = d;
+    pp.sqh = (long long)a.Nq * d;
+    pp.sqb = (long long)a.Hq * a.Nq * d;
+  }
+  pp.table = a.block_table;
+  pp.max_blocks = a.max_blocks;
+  pp.num_blocks = a.num_blocks;
+  pp.max_len = a.max_len;
+  pp.seq_lens = a.seq_lens;
   const long long nblocks = (long long)pp.n_qblk * a.B * a.Hkv * pp.n_hgrp;
   if (nblocks <= 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.d == 128)
-    return a.causal ? launch_typed<128, true>(pp, (int)nblocks, s)
-                    : launch_typed<128, false>(pp, (int)nblocks, s);
-  return a.causal ? launch_typed<64, true>(pp, (int)nblocks, s)
-                  : launch_typed<64, false>(pp, (int)nblocks, s);
+  const bool cache = a.cache != 0;
+  if (a.d == 128) return launch_d<128>(pp, a.causal, cache, (int)nblocks, s);
+  return launch_d<64>(pp, a.causal, cache, (int)nblocks, s);
 }
 
 }  // namespace attn

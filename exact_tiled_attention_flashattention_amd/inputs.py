@@ -31,6 +31,10 @@ WORKLOADS = {
                                d=128, seq_len=32768, dtype="bf16"),
     "paged_decode_q4": dict(seed=1005, kind="decode_paged", B=32, Hq=32, Hkv=8, Nq=4, d=128,
                             len_lo=1024, len_hi=16384, dtype="bf16"),
+    # chunked prefill: a 512-token chunk per sequence appended after a cached
+    # prefix, then attending to the whole paged cache
+    "chunked_prefill_paged": dict(seed=1006, kind="prefill_paged", B=8, Hq=32, Hkv=8, Nq=512,
+                                  d=128, len_lo=1024, len_hi=8192, dtype="bf16"),
 }
 
 

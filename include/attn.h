@@ -79,6 +79,38 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, int q_offset, void* stream);
 
 /*
+ * Chunked prefill against a K/V cache: the Nq new tokens of each sequence
+ * attend to every cached key, including their own rows, which kv_append has
+ * already written ("Phase 07 · 12", section "Paged attention": reusing the
+ * cached K/V of a shared prefix; the new chunk's rows follow the cached ones,
+ * so its causal mask is offset by the cached length, "Effizienz", "Der
+ * wichtige Maskenfehler beim Cache"). Same arguments and cache layouts as
+ * attn_decode_paged, for any Nq (the tiled MFMA path of attn_prefill; no
+ * workspace):
+ *   q, o        : [B, Nq, Hq, d] bf16
+ *   lse         : [B, Hq, Nq] f32, or NULL to skip it
+ *   paged cache : block_table != NULL; k_cache, v_cache are pools
+ *                 [num_blocks, 16, Hkv, d], block_table [B, max_blocks_per_seq]
+ *                 int32, token t of sequence b in block block_table[b][t / 16],
+ *                 slot t % 16
+ *   contiguous  : block_table == NULL; k_cache, v_cache are
+ *                 [B, max_seq_len, Hkv, d]
+ *   seq_lens    : [B] int32, keys of sequence b including its Nq new ones;
+ *                 clamped to [0, max_seq_len] (and max_blocks_per_seq·16 when
+ *                 paged). Query row i of sequence b sits at position
+ *                 seq_lens[b] - Nq + i; with causal it sees keys j <= that
+ *                 position, without causal all seq_lens[b] keys. Rows before
+ *                 position 0 see no key (O = 0, LSE = -inf). Table entries
+ *                 outside [0, num_blocks) make their 16 keys invisible.
+ * Supported: dtype ATTN_BF16, d in {64, 128}, 16·Hkv·d·2 < 2^31.
+ */
+int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                       const int32_t* seq_lens, void* o, float* lse,
+                       int dtype, int B, int Hq, int Hkv, int Nq, int d,
+                       float scale, int causal, int max_seq_len, void* stream);
+
+/*
  * Decode of Nq new tokens per sequence against a K/V cache, split along the
  * key sequence (Flash-Decoding, "[BEE-30062]" Background) and merged with a
  * log-sum-exp combine.

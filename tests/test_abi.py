@@ -30,7 +30,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("attn_prefill", "attn_decode_paged", "kv_append", "attn_decode_workspace_bytes",
+    for n in ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "kv_append",
+              "attn_decode_workspace_bytes",
               "attn_decode_num_splits", "attn_gather_paged", "attn_strerror"):
         assert n in names
 
@@ -155,3 +156,46 @@ def test_kv_append_and_gather_reject():
     assert lib.attn_gather_paged(FAKE, FAKE, 0, 4, FAKE, FAKE, 1, 1, 2, 128, 16, None) == -1
     # nothing to do
     assert lib.kv_append(FAKE, FAKE, FAKE, FAKE, None, 0, 0, FAKE, 1, 0, 2, 1, 128, 16, None) == 0
+
+
+def _prefill_paged(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=None, mb=0, nb=0, sl=FAKE, o=FAKE, lse=None, dtype=1, B=2,
+             Hq=32, Hkv=8, Nq=512, d=128, scale=0.1, causal=1, L=4096)
+    a.update(kw)
+    return eta.library().attn_prefill_paged(a["q"], a["k"], a["v"], a["bt"], a["mb"], a["nb"],
+                                            a["sl"], a["o"], a["lse"], a["dtype"], a["B"], a["Hq"],
+                                            a["Hkv"], a["Nq"], a["d"], a["scale"], a["causal"],
+                                            a["L"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), eta.ATTN_EUNSUPPORTED),       # fp32 cache prefill not built
+    (dict(d=80), eta.ATTN_EUNSUPPORTED),
+    (dict(Hkv=1 << 20), eta.ATTN_EINVAL),         # Hq % Hkv != 0
+    (dict(Hq=30), eta.ATTN_EINVAL),
+    (dict(L=-1), eta.ATTN_EINVAL),
+    (dict(Nq=-1), eta.ATTN_EINVAL),
+    (dict(sl=None), eta.ATTN_EINVAL),
+    (dict(q=None), eta.ATTN_EINVAL),
+    (dict(bt=FAKE, mb=0), eta.ATTN_EINVAL),
+    (dict(bt=FAKE, mb=4, nb=-1), eta.ATTN_EINVAL),
+    (dict(scale=float("nan")), eta.ATTN_EINVAL),
+    (dict(scale=-1.0), eta.ATTN_EINVAL),
+    (dict(q=P(0x10002)), eta.ATTN_EINVAL),        # misaligned
+    (dict(Hq=(1 << 19), Hkv=(1 << 19)), eta.ATTN_EUNSUPPORTED),  # 16*Hkv*d*2 >= 2^31
+])
+def test_prefill_paged_rejects(kw, code):
+    assert _prefill_paged(**kw) == code
+
+
+def test_prefill_paged_empty_is_a_no_op():
+    # nothing to compute: returns before touching any (fake) pointer
+    assert _prefill_paged(B=0) == eta.ATTN_OK
+    assert _prefill_paged(Nq=0) == eta.ATTN_OK
+
+
+def test_prefill_rejects_key_counts_past_32_bit_offsets():
+    lib = eta.library()
+    st = lib.attn_prefill(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 8, 8, 16, (1 << 22) + 1, 128, 0.1, 1,
+                          0, None)
+    assert st == eta.ATTN_EUNSUPPORTED

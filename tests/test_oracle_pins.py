@@ -242,11 +242,13 @@ def test_decode_rows_equal_last_rows_of_full_prefill():
     assert np.abs(Owrong - Ofull[:, :, n - Nq:]).max() > 1e-3
 
 
-@pytest.mark.parametrize("step", [1, 4])
+@pytest.mark.parametrize("step", [1, 4, 17, 40])
 def test_cached_paged_decode_equals_full_recompute(step):
     # "Phase 07 · 12" exercise 1 and "Effizienz" extension plan: decode with a
     # growing (here paged) cache, each K/V appended once, and compare every
-    # position with a full causal recompute.
+    # position with a full causal recompute. Steps of 17 (chunks that straddle
+    # 16-token blocks, ragged last chunk) and 40 (the whole prompt as one
+    # chunk) are chunked prefill against the paged cache.
     n, Hq, Hkv, d = 40, 4, 2, 8
     q = _rand((1, Hq, n, d), 26)
     k = _rand((1, Hkv, n, d), 27)
