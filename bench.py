@@ -162,7 +162,7 @@ def counter_traffic(stage, kernel, sources):
     return None
 
 
-def cpu_baseline(q, k, v, min_seconds=10.0, max_heads=64):
+def cpu_baseline(q, k, v, min_seconds=10.0, max_heads=128):
     """Time the fp64 oracle on whole heads (all 4096 rows) of the 4k causal prefill,
     cycling over the 32 heads until about `min_seconds` of CPU work is done."""
     import numpy as np
@@ -352,12 +352,12 @@ def main():
     torch.cuda.synchronize()
     result_workloads["single_head_f32"] = {"us": round(t1.mean_ms("p") * 1e3, 2)}
 
-    traffic = counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true>",
+    traffic = counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true,false>",
                               ["common.h", "prefill_bf16.hip"])
     roofline = {"bound": "mfma", "achieved": round(tflops2, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops2 / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "traffic_unit": "bytes per launch (HBM read + write)",
-                "kernel": "prefill_bf16_kernel<128, causal>",
+                "kernel": "prefill_bf16_kernel<128, causal, slabs>",
                 "per_launch": f"{flops2:.6g} FLOP (visible pairs x 4d) per launch"}
 
     cpu = None

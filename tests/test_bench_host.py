@@ -31,9 +31,9 @@ def test_causal_pair_count_matches_the_oracle_mask():
 
 
 def test_counter_traffic_is_null_for_other_sources():
-    got = bench.counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true>",
+    got = bench.counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true,false>",
                                 ["common.h", "prefill_bf16.hip"])
     assert got is None or (isinstance(got, int) and got > 0)
-    assert bench.counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true>",
+    assert bench.counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true,false>",
                                  ["common.h", "kv_cache.hip"]) is None
     assert bench.counter_traffic("no_such_stage", "x", ["common.h"]) is None
