@@ -28,6 +28,9 @@ exists at once in fp64 and the softmax sees the whole row. Sources:
   "Cachebedarf berechnen" (M_KV = 2·L·B·T·Hkv·d·e) and "Der wichtige
   Maskenfehler beim Cache" (the causal mask must carry a position offset when
   the query is shorter than the keys).
+* fp8.py: the E4M3 encoding of a quantised K/V cache with per-head scales
+  (the fp8 cache option of "Phase 07 · 12", section "Paged attention"; the
+  encoding is the OCP 8-bit format, a reading stated in that module).
 
 Every function here is pinned by CPU tests against values and identities that
 the pages and the mathematics fix (tests/test_oracle_*.py); none is marked
@@ -44,6 +47,7 @@ from .attention import (
 from .paged import gather_paged, gather_contiguous, kv_append_ref
 from .online import online_attention_rows
 from .counts import kv_cache_bytes, visible_pairs, naive_vs_cached_kv_states
+from .fp8 import E4M3_MAX, e4m3_decode, e4m3_encode, quantize, dequantize
 
 __all__ = [
     "NEG_INF",
@@ -58,4 +62,9 @@ __all__ = [
     "kv_cache_bytes",
     "visible_pairs",
     "naive_vs_cached_kv_states",
+    "E4M3_MAX",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize",
+    "dequantize",
 ]

@@ -89,3 +89,36 @@ def test_pin_catches_wrong_append_slot(monkeypatch):
     _install(monkeypatch, mod, ("kv_append_ref",), (oracle, opaged))
     with pytest.raises(AssertionError):
         pins.test_kv_append_round_trip_and_untouched_bytes()
+
+
+import oracle.fp8 as ofp8  # noqa: E402
+from tests import test_oracle_fp8 as fp8pins  # noqa: E402
+
+FP8 = ("e4m3_decode", "e4m3_encode", "quantize", "dequantize")
+
+FP8_MUTANTS = [
+    ("exponent bias 8 (the FNUZ variant)",
+     "flat_o[i] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
+     "flat_o[i] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)",
+     fp8pins.test_decode_matches_torch_for_every_code),
+    ("ties away from zero",
+     "even = [int(t) for t in ties if int(_POS_CODES[t]) % 2 == 0]",
+     "even = [int(t) for t in ties][::-1]",
+     fp8pins.test_closed_forms),
+    ("no saturation beyond 448",
+     "a = min(abs(v), E4M3_MAX)",
+     "a = abs(v) if abs(v) <= E4M3_MAX else float('nan')",
+     fp8pins.test_closed_forms),
+    ("scale multiplied instead of divided",
+     "y = (xf / s).astype(np.float32)",
+     "y = (xf * s).astype(np.float32)",
+     fp8pins.test_quantisation_error_bound),
+]
+
+
+@pytest.mark.parametrize("label,old,new,pin", FP8_MUTANTS, ids=[m[0] for m in FP8_MUTANTS])
+def test_pin_catches_fp8_mutant(monkeypatch, label, old, new, pin):
+    mod = _mutant("fp8.py", old, new)
+    _install(monkeypatch, mod, FP8, (oracle, ofp8))
+    with pytest.raises((AssertionError, ValueError)):
+        pin()
