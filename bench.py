@@ -11,8 +11,9 @@ seeded workload with inputs already resident in HBM:
   * split-KV decode of 1 token against 16 contiguous 32768-token caches.
 Each stage is timed with HIP events recorded on the stream the library
 launches on; the long-context prefill (N=32768), the chunked prefill against
-the paged cache (8 sequences, 512 new tokens after 1k-8k cached ones) and the
-fp32 single-head case are timed in their own loops after the steps. FLOPs count visible
+the paged cache (8 sequences, 512 new tokens after 1k-8k cached ones), the
+paged 4-token decode over an fp8 (E4M3) cache and the fp32 single-head case
+are timed in their own loops after the steps. FLOPs count visible
 (query, key) pairs x 4d; decode bytes count each visible K/V row once.
 Prints ONE JSON line.
 """
@@ -62,7 +63,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage", default=None,
                     choices=["prefill_4k", "prefill_32k", "splitkv_decode_32k", "paged_decode_q4",
-                             "chunked_prefill_paged", "copy_1gib"],
+                             "chunked_prefill_paged", "paged_decode_q4_fp8", "copy_1gib"],
                     help="run only this stage --steps times and exit (for profiler runs); "
                          "copy_1gib is a plain 1 GiB device copy used to calibrate HBM counters")
     return ap.parse_args()
@@ -87,6 +88,13 @@ def run_stage(args, torch, eta, inputs, dev):
                       block_table=p["block_table"])
         fn = lambda: eta.attn_prefill_paged(p["q"], p["k_pool"], p["v_pool"], p["seq_lens"],  # noqa
                                             block_table=p["block_table"], causal=True)
+    elif name == "paged_decode_q4_fp8":
+        p = inputs.workload_inputs(name, dev)
+        eta.kv_append_fp8(p["k_new"], p["v_new"], p["k_pool"], p["v_pool"], p["k_scale"],
+                          p["v_scale"], p["cache_lens"], block_table=p["block_table"])
+        fn = lambda: eta.attn_decode_paged_fp8(p["q"], p["k_pool"], p["v_pool"], p["k_scale"],  # noqa
+                                               p["v_scale"], p["seq_lens"],
+                                               block_table=p["block_table"], causal=True)
     elif name == "splitkv_decode_32k":
         q, kc, vc, sl = inputs.workload_inputs(name, dev)
         fn = lambda: eta.attn_decode_paged(q, kc, vc, sl, causal=True)  # noqa: E731
@@ -342,6 +350,42 @@ def main():
         "frac_of_peak": round(flops6 / (ms6 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops": flops6}
     del p6, o6, l6
+    torch.cuda.empty_cache()
+    # the paged 4-token decode over an E4M3 cache (one byte per element)
+    w7 = inputs.WORKLOADS["paged_decode_q4_fp8"]
+    p7 = inputs.workload_inputs("paged_decode_q4_fp8", dev)
+    L7 = p7["block_table"].shape[1] * 16
+    o7 = torch.empty_like(p7["q"])
+    l7 = torch.empty((w7["B"], w7["Hq"], w7["Nq"]), dtype=torch.float32, device=dev)
+    ws7 = torch.empty(eta.attn_decode_workspace_bytes(w7["B"], w7["Hq"], w7["Hkv"], w7["Nq"],
+                                                      w7["d"], L7), dtype=torch.uint8, device=dev)
+    seq7 = [int(x) for x in p7["seq_lens"].cpu()]
+
+    def append7():
+        eta.kv_append_fp8(p7["k_new"], p7["v_new"], p7["k_pool"], p7["v_pool"], p7["k_scale"],
+                          p7["v_scale"], p7["cache_lens"], block_table=p7["block_table"])
+
+    def decode7():
+        eta.attn_decode_paged_fp8(p7["q"], p7["k_pool"], p7["v_pool"], p7["k_scale"],
+                                  p7["v_scale"], p7["seq_lens"], block_table=p7["block_table"],
+                                  causal=True, workspace=ws7, out=o7, lse=l7)
+
+    t7 = StageTimer(torch, stream, ["a", "d"])
+    for _ in range(3):
+        append7()
+        decode7()
+    for _ in range(20):
+        t7.run("a", append7)
+        t7.run("d", decode7)
+    torch.cuda.synchronize()
+    ms7 = t7.mean_ms("d")
+    bytes7 = 2 * 1 * w7["Hkv"] * w7["d"] * sum(seq7)
+    result_workloads["paged_decode_q4_fp8"] = {
+        "ms": round(ms7, 5), "GB/s": round(bytes7 / (ms7 * 1e-3) / 1e9, 1),
+        "frac_of_peak": round(bytes7 / (ms7 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+        "kv_bytes": bytes7, "kv_append_ms": round(t7.mean_ms("a"), 5),
+        "speedup_vs_bf16_cache": round(ms5 / ms7, 3)}
+    del p7, o7, l7, ws7
     torch.cuda.empty_cache()
     q1, k1, v1 = inputs.workload_inputs("single_head_f32", dev)
     t1 = StageTimer(torch, stream, ["p"])

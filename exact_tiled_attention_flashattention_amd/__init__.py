@@ -56,6 +56,11 @@ def _load():
     lib.attn_prefill.restype = I
     lib.attn_prefill_paged.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill_paged.restype = I
+    lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, I, I, P, P, P, I, I, I, I, I, F, I, I,
+                                          I, P, SZ, P]
+    lib.attn_decode_paged_fp8.restype = I
+    lib.kv_append_fp8.argtypes = [P, P, P, P, P, P, P, I, I, P, I, I, I, I, I, P]
+    lib.kv_append_fp8.restype = I
     lib.attn_decode_paged.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I, I, I,
                                       P, SZ, P]
     lib.attn_decode_paged.restype = I
@@ -254,6 +259,87 @@ def kv_append(k_new, v_new, k_cache, v_cache, cache_lens, block_table=None, max_
     _check(st, "kv_append")
 
 
+def _fp8_cache(t):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("an fp8 cache is uint8 (E4M3 codes) or float8_e4m3fn")
+
+
+def _scales(s, Hkv, device):
+    if s.dtype != torch.float32 or s.shape != (Hkv,) or s.device != device:
+        raise ValueError("scales must be float32 [Hkv] on the cache's device")
+
+
+def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_lens, block_table=None,
+                  max_seq_len=None):
+    """Quantise k_new/v_new [B,Nnew,Hkv,d] (bf16) into an E4M3 cache at positions
+    cache_lens[b] + r (in place); code = nearest(x / scale[h]), saturating at 448."""
+    lib = _load()
+    _need_gpu(k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_lens, block_table)
+    B, Nnew, Hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or k_cache.shape[2:] != (Hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between new rows and cache")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("new rows are bf16")
+    _fp8_cache(k_cache)
+    _fp8_cache(v_cache)
+    _scales(k_scale, Hkv, k_cache.device)
+    _scales(v_scale, Hkv, k_cache.device)
+    if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,):
+        raise ValueError("cache_lens must be int32 [B]")
+    L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    st = lib.kv_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                           _ptr(v_scale), _ptr(block_table), mb, nblocks, _ptr(cache_lens), B, Hkv,
+                           Nnew, d, L, _stream(k_new.device))
+    _check(st, "kv_append_fp8")
+
+
+def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table=None,
+                          scale=None, causal=True, max_seq_len=None, num_splits=0, workspace=None,
+                          out=None, lse=None, want_lse=True):
+    """Decode against an E4M3 cache with per-head scales. q [B,Nq,Hq,d] bf16; caches
+    uint8 [P,16,Hkv,d] (paged) or [B,L,Hkv,d]; -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
+    lib = _load()
+    _need_gpu(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table)
+    B, Nq, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must share a shape with head dim d")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("q is bf16")
+    _fp8_cache(k_cache)
+    _fp8_cache(v_cache)
+    _scales(k_scale, Hkv, q.device)
+    _scales(v_scale, Hkv, q.device)
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B, max_blocks]")
+        if k_cache.shape[1] != BLOCK_TOKENS:
+            raise ValueError("a paged cache is [num_blocks, 16, Hkv, d]")
+    elif k_cache.shape[0] != B:
+        raise ValueError("a contiguous cache is [B, max_len, Hkv, d]")
+    L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, L, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _need_gpu(workspace, out, lse)
+    st = lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                   _ptr(v_scale), _ptr(block_table), mb, nblocks, _ptr(seq_lens),
+                                   _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, d, float(scale),
+                                   int(bool(causal)), L, int(num_splits), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _stream(q.device))
+    _check(st, "attn_decode_paged_fp8")
+    return out, lse
+
+
 def attn_gather_paged(cache, seq_lens, block_table=None, max_seq_len=None, out=None):
     """Gather each sequence's first seq_lens[b] rows into out [B, max_seq_len, Hkv, d]."""
     lib = _load()
@@ -273,6 +359,8 @@ def attn_gather_paged(cache, seq_lens, block_table=None, max_seq_len=None, out=N
 __all__ = [
     "attn_prefill",
     "attn_prefill_paged",
+    "attn_decode_paged_fp8",
+    "kv_append_fp8",
     "attn_decode_paged",
     "attn_decode_num_splits",
     "attn_decode_workspace_bytes",

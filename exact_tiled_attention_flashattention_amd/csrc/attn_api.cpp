@@ -184,18 +184,24 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int ma
   return workspace_layout(B, Hq, Hkv, Nq, d, plan_workers(num_splits, Hq, Hkv, Nq)).total;
 }
 
-int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
-                      const int32_t* seq_lens, void* o, float* lse, int dtype, int B, int Hq,
-                      int Hkv, int Nq, int d, float scale, int causal, int max_seq_len,
-                      int num_splits, void* workspace, size_t workspace_bytes_given,
-                      void* stream) {
+}  // extern "C"
+
+static int decode_impl(const void* q, const void* k_cache, const void* v_cache, int kv8,
+                       const float* k_scale, const float* v_scale, const int32_t* block_table,
+                       int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens, void* o,
+                       float* lse, int dtype, int B, int Hq, int Hkv, int Nq, int d, float scale,
+                       int causal, int max_seq_len, int num_splits, void* workspace,
+                       size_t workspace_bytes_given, void* stream) {
   const int st = check_decode_shape(dtype, B, Hq, Hkv, Nq, d, max_seq_len, num_splits);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
   if (block_table != nullptr && (max_blocks_per_seq <= 0 || num_blocks < 0)) return ATTN_EINVAL;
   if (B == 0 || Nq == 0) return ATTN_OK;
   if (q == nullptr || o == nullptr || seq_lens == nullptr) return ATTN_EINVAL;
+  if (kv8 && (k_scale == nullptr || v_scale == nullptr ||
+              (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+              (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
+    return ATTN_EINVAL;
   if (max_seq_len > 0 && (k_cache == nullptr || v_cache == nullptr)) return ATTN_EINVAL;
   if (misaligned16(q) || misaligned16(o) || misaligned16(k_cache) || misaligned16(v_cache) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
@@ -224,11 +230,39 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   a.causal = causal != 0;
   a.max_seq_len = max_seq_len;
   a.workers = workers;
+  a.kv8 = kv8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   char* ws = static_cast<char*>(workspace);
   a.part_o = reinterpret_cast<float*>(ws);
   a.part_lse = reinterpret_cast<float*>(ws + lay.part_lse_off);
   a.prefix = reinterpret_cast<long long*>(ws + lay.prefix_off);
   return status_of(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                      const int32_t* seq_lens, void* o, float* lse, int dtype, int B, int Hq,
+                      int Hkv, int Nq, int d, float scale, int causal, int max_seq_len,
+                      int num_splits, void* workspace, size_t workspace_bytes_given,
+                      void* stream) {
+  return decode_impl(q, k_cache, v_cache, 0, nullptr, nullptr, block_table, max_blocks_per_seq,
+                     num_blocks, seq_lens, o, lse, dtype, B, Hq, Hkv, Nq, d, scale, causal,
+                     max_seq_len, num_splits, workspace, workspace_bytes_given, stream);
+}
+
+int attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                          const int32_t* seq_lens, void* o, float* lse, int B, int Hq, int Hkv,
+                          int Nq, int d, float scale, int causal, int max_seq_len,
+                          int num_splits, void* workspace, size_t workspace_bytes_given,
+                          void* stream) {
+  return decode_impl(q, k_cache, v_cache, 1, k_scale, v_scale, block_table, max_blocks_per_seq,
+                     num_blocks, seq_lens, o, lse, ATTN_BF16, B, Hq, Hkv, Nq, d, scale, causal,
+                     max_seq_len, num_splits, workspace, workspace_bytes_given, stream);
 }
 
 static int check_copy(const void* a, const void* b, const int32_t* block_table,
@@ -272,6 +306,39 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
   a.d = d;
   a.max_seq_len = max_seq_len;
   return status_of(attn::launch_kv_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                  int max_blocks_per_seq, int num_blocks, const int32_t* cache_lens, int B,
+                  int Hkv, int Nnew, int d, int max_seq_len, void* stream) {
+  int st = check_copy(k_new, v_new, block_table, max_blocks_per_seq, num_blocks, cache_lens,
+                      ATTN_BF16, B, Hkv, Nnew, d, max_seq_len);
+  if (st <= 0) return st;
+  if (k_scale == nullptr || v_scale == nullptr || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+    return ATTN_EINVAL;
+  if (max_seq_len == 0) return ATTN_OK;  // no position can be written
+  if (k_cache == nullptr || v_cache == nullptr || misaligned16(k_cache) || misaligned16(v_cache))
+    return ATTN_EINVAL;
+  attn::CacheCopyArgs a;
+  a.src_k = k_new;
+  a.src_v = v_new;
+  a.dst_k = k_cache;
+  a.dst_v = v_cache;
+  a.block_table = block_table;
+  a.max_blocks = block_table ? max_blocks_per_seq : 0;
+  a.num_blocks = block_table ? num_blocks : 0;
+  a.lens = cache_lens;
+  a.elem_bytes = 2;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.Nnew = Nnew;
+  a.d = d;
+  a.max_seq_len = max_seq_len;
+  return status_of(attn::launch_kv_append_fp8(a, static_cast<hipStream_t>(stream)));
 }
 
 int attn_gather_paged(const void* cache, const int32_t* block_table, int max_blocks_per_seq,

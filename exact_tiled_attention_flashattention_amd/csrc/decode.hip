@@ -1,4 +1,5 @@
-// Split-KV decode against a paged or contiguous cache, bf16, gfx950.
+// Split-KV decode against a paged or contiguous cache of bf16 or E4M3 codes,
+// gfx950.
 //
 // Method: Flash-Decoding ("[BEE-30062] FlashAttention 與高效注意力核心",
 // Background): during decode the batch and the query length are small, so
@@ -51,8 +52,10 @@ namespace {
 
 struct DecodeParams {
   const __bf16* q;
-  const __bf16* k;
-  const __bf16* v;
+  const char* k;          // cache bytes: bf16, or E4M3 codes (KV8)
+  const char* v;
+  const float* ksc;       // KV8: per-K/V-head scales of the codes
+  const float* vsc;
   CacheView cv;
   const int32_t* seq_lens;
   __bf16* o;
@@ -108,12 +111,27 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {
 constexpr float kTau = 8.0f;               // rescale only when a row max grows by more than 2^8
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, 32-bit dword data
 
-// K/V of one 32-key step, in the registers the MFMAs consume.
+// K/V of one 32-key step as loaded.
+template <int D, bool KV8>
+struct StepRegs;
 template <int D>
-struct StepRegs {
-  bf16x8_t kf[2][D / 32];  // A operand of Sᵀ: lane = key (r16) of half h2, 8 d at 32c + 8g
-  u32x4_t vv[2][4];        // 8 d (chunk r16) of keys 16*h2 + 4*g + jj
+struct StepRegs<D, false> {  // bf16: already the MFMA operands
+  bf16x8_t kf[2][D / 32];    // A operand of Sᵀ: lane = key (r16) of half h2, 8 d at 32c + 8g
+  u32x4_t vv[2][4];          // 8 d (chunk r16) of keys 16*h2 + 4*g + jj
 };
+template <int D>
+struct StepRegs<D, true> {  // E4M3 codes, widened to bf16 where they are used
+  u32x4_t kq[2][D / 64];    // key r16 of half h2, 16 d at 64*c2 + 16*g
+  u32x2_t vq[2][4];         // 8 d (d = 8*r16 ...) of keys 16*h2 + 4*g + jj
+};
+
+// two E4M3 codes (bytes 2*hi, 2*hi+1 of w) as a bf16 pair packed in a dword;
+// E4M3 values are exact in bf16
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
 
 // One 16-token stretch of one K/V head as a buffer resource whose range ends
 // after its last valid row: loads past it (tokens beyond the sequence, a
@@ -123,8 +141,16 @@ struct Span {
   bool ok;  // the stretch has storage (its keys may be visible)
 };
 
-template <int D>
+#ifndef ATTN_FP8_DEPTH
+#define ATTN_FP8_DEPTH 3
+#endif
+
+template <int D, bool KV8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_partial_kernel(DecodeParams p) {
+  constexpr int EB = KV8 ? 1 : 2;  // bytes per cached element
+  // steps in the pipeline: an E4M3 step is half the bytes, so it keeps more
+  // of them in flight
+  constexpr int DEPTH = KV8 ? ATTN_FP8_DEPTH : 2;
   constexpr int NC = D / 32;  // MFMAs per 16 keys for Sᵀ (32 d each)
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;  // query row (Sᵀ/Oᵀ column) of this lane
@@ -181,10 +207,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   b = __builtin_amdgcn_readfirstlane(b);
 
-  const int rowb = p.cv.hkv * D * 2;  // bytes between consecutive tokens of one head
+  const int rowb = p.cv.hkv * D * EB;  // bytes between consecutive tokens of one head
   // loop-invariant lane byte offsets inside a 16-token stretch
-  const int koff = r16 * rowb + 16 * g;         // K: token r16, d = 8*g (+32c via imm)
-  const int voff = (4 * g) * rowb + 16 * r16;   // V: token 4*g (+jj via soffset), chunk r16
+  // K: token r16, 16 bytes at 16*g (+64 per further load); V: token 4*g (+jj
+  // via soffset), the 8 d from 8*r16
+  const int koff = r16 * rowb + 16 * g;
+  const int voff = (4 * g) * rowb + 8 * EB * r16;
   const int row = 16 * rg + r16;                // rows r = qi * G + h, r < M
   const bool row_ok = r16 < p.MP && row < p.M;
   const int qi = row_ok ? row / p.G : 0;
@@ -198,15 +226,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int limit = ke;  // keys of this piece visible to the row: [kb0, limit)
     if (p.causal) limit = min(limit, n - p.Nq + qi + 1);
 
-    // Qᵀ as the B operand: lane holds row r16, d = 32*c + 8*g + j
+    // Qᵀ as the B operand: lane holds row r16 and, for MFMA c, the 8 d that
+    // the K operand of lane group g holds: d = 32*c + 8*g + j (bf16 cache) or
+    // d = 64*(c/2) + 16*g + 8*(c%2) + j (E4M3 cache: one 16-byte load per
+    // lane holds two MFMAs' worth of K)
     bf16x8_t qf[NC];
     {
       const __bf16* qp =
-          p.q + (((long long)b * p.Nq + qi) * p.Hq + (long long)kvh * p.G + hrow) * D + 8 * g;
+          p.q + (((long long)b * p.Nq + qi) * p.Hq + (long long)kvh * p.G + hrow) * D;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qp + 32 * c) : bf16x8_t{};
+      for (int c = 0; c < NC; ++c) {
+        const int d0 = KV8 ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
+        qf[c] = row_ok ? *reinterpret_cast<const bf16x8_t*>(qp + d0) : bf16x8_t{};
+      }
     }
+    // score scale in base 2, and the factor of O; E4M3 codes carry per-head scales
+    const float cs = KV8 ? p.c * p.ksc[kvh] : p.c;
+    const float os = KV8 ? p.vsc[kvh] : 1.f;
 
     f32x4_t acc[8];
 #pragma unroll
@@ -240,28 +276,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
       sp.ok = row >= 0;
-      const long long base = sp.ok ? row + (long long)kvh * D : 0;
-      const int bytes = sp.ok ? (valid - 1) * rowb + D * 2 : 0;
+      const long long base = sp.ok ? (row + (long long)kvh * D) * EB : 0;
+      const int bytes = sp.ok ? (valid - 1) * rowb + D * EB : 0;
       sp.k = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + base), 0, bytes, kBufferFlags);
       sp.v = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + base), 0, bytes, kBufferFlags);
       return sp;
     };
 
-    auto load = [&](const Span (&sp)[2], StepRegs<D>& r) __attribute__((always_inline)) {
+    auto load = [&](const Span (&sp)[2], StepRegs<D, KV8>& r) __attribute__((always_inline)) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
+        if constexpr (KV8) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          r.kf[h2][c] = __builtin_bit_cast(
-              bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].k, koff + 64 * c, 0, 0));
+          for (int c2 = 0; c2 < D / 64; ++c2)
+            r.kq[h2][c2] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].k, koff + 64 * c2, 0, 0));
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          r.vv[h2][jj] = __builtin_bit_cast(
-              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].v, voff, jj * rowb, 0));
+          for (int jj = 0; jj < 4; ++jj)
+            r.vq[h2][jj] = __builtin_bit_cast(
+                u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(sp[h2].v, voff, jj * rowb, 0));
+        } else {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            r.kf[h2][c] = __builtin_bit_cast(
+                bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].k, koff + 64 * c, 0, 0));
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            r.vv[h2][jj] = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sp[h2].v, voff, jj * rowb, 0));
+        }
+      }
+    };
+    // the MFMA operands of a step: K fragment (h2, c) and V chunk (h2, jj)
+    auto kfrag = [&](const StepRegs<D, KV8>& r, int h2, int c) __attribute__((always_inline)) {
+      if constexpr (KV8) {
+        const u32x4_t w = r.kq[h2][c >> 1];
+        const uint32_t w0 = (c & 1) ? w[2] : w[0];
+        const uint32_t w1 = (c & 1) ? w[3] : w[1];
+        const u32x4_t f = {fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                           fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
+        return __builtin_bit_cast(bf16x8_t, f);
+      } else {
+        return r.kf[h2][c];
+      }
+    };
+    auto vchunk = [&](const StepRegs<D, KV8>& r, int h2, int jj) __attribute__((always_inline)) {
+      if constexpr (KV8) {
+        const u32x2_t w = r.vq[h2][jj];
+        const u32x4_t f = {fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]),
+                           fp8x2_to_bf16x2<false>(w[1]), fp8x2_to_bf16x2<true>(w[1])};
+        return f;
+      } else {
+        return r.vv[h2][jj];
       }
     };
 
-    auto compute = [&](int k0, const Span (&sp)[2], const StepRegs<D>& r)
+    auto compute = [&](int k0, const Span (&sp)[2], const StepRegs<D, KV8>& r)
         __attribute__((always_inline)) {
       f32x4_t s[2];
 #pragma unroll
@@ -269,7 +339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         s[h2] = f32x4_t{};
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.kf[h2][c], qf[c], s[h2], 0, 0, 0);
+          s[h2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(r, h2, c), qf[c], s[h2], 0, 0, 0);
       }
       float mx = neg_inf();
 #pragma unroll
@@ -282,7 +352,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       mx = max_across_rows16(mx);
       mx = max_across_halves(mx);
-      const float mt = mx * p.c;
+      const float mt = mx * cs;
       // the reference max only moves (and O, l are rescaled) when the row max
       // jumps by more than kTau
       const bool need = mt > m_run + kTau;
@@ -300,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h2][i], p.c, -m_use));
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h2][i], cs, -m_use));
           s[h2][i] = e;
           rs += e;
         }
@@ -310,17 +380,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const bf16x4_t p0 = __builtin_convertvector(s[0], bf16x4_t);
       const bf16x4_t p1 = __builtin_convertvector(s[1], bf16x4_t);
       const bf16x8_t pb8 = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      u32x4_t vv[2][4];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) vv[h2][jj] = vchunk(r, h2, jj);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {  // dword e of each V chunk holds d = 8*r16 + 2e, 2e+1
         u32x4_t lo, hi;
-        lo[0] = perm_lo(r.vv[0][0][e], r.vv[0][1][e]);
-        lo[1] = perm_lo(r.vv[0][2][e], r.vv[0][3][e]);
-        lo[2] = perm_lo(r.vv[1][0][e], r.vv[1][1][e]);
-        lo[3] = perm_lo(r.vv[1][2][e], r.vv[1][3][e]);
-        hi[0] = perm_hi(r.vv[0][0][e], r.vv[0][1][e]);
-        hi[1] = perm_hi(r.vv[0][2][e], r.vv[0][3][e]);
-        hi[2] = perm_hi(r.vv[1][0][e], r.vv[1][1][e]);
-        hi[3] = perm_hi(r.vv[1][2][e], r.vv[1][3][e]);
+        lo[0] = perm_lo(vv[0][0][e], vv[0][1][e]);
+        lo[1] = perm_lo(vv[0][2][e], vv[0][3][e]);
+        lo[2] = perm_lo(vv[1][0][e], vv[1][1][e]);
+        lo[3] = perm_lo(vv[1][2][e], vv[1][3][e]);
+        hi[0] = perm_hi(vv[0][0][e], vv[0][1][e]);
+        hi[1] = perm_hi(vv[0][2][e], vv[0][3][e]);
+        hi[2] = perm_hi(vv[1][0][e], vv[1][1][e]);
+        hi[3] = perm_hi(vv[1][2][e], vv[1][3][e]);
         acc[2 * e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lo),
                                                              pb8, acc[2 * e], 0, 0, 0);
         acc[2 * e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hi),
@@ -328,35 +403,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     };
 
-    // software pipeline: the next step's block lookups and loads are issued
-    // before the current step is computed
-    StepRegs<D> ra, rb;
-    Span sa[2], sb[2];
-    sa[0] = span(kb0);
-    sa[1] = span(kb0 + 16);
-    load(sa, ra);
-    for (int k0 = kb0; k0 < ke; k0 += 64) {
-      const bool more1 = k0 + 32 < ke;
-      if (more1) {
-        sb[0] = span(k0 + 32);
-        sb[1] = span(k0 + 48);
-        load(sb, rb);
+    // software pipeline: the block lookups and loads of step k+DEPTH-1 are
+    // issued (into the registers step k-1 has just released) before step k
+    // is computed, so DEPTH-1 steps of K/V are in flight per wave
+    StepRegs<D, KV8> r[DEPTH];
+    Span sp[DEPTH][2];
+#pragma unroll
+    for (int j = 0; j + 1 < DEPTH; ++j) {
+      if (kb0 + 32 * j < ke) {
+        sp[j][0] = span(kb0 + 32 * j);
+        sp[j][1] = span(kb0 + 32 * j + 16);
+        load(sp[j], r[j]);
       }
-      compute(k0, sa, ra);
-      if (!more1) break;
-      const bool more2 = k0 + 64 < ke;
-      if (more2) {
-        sa[0] = span(k0 + 64);
-        sa[1] = span(k0 + 80);
-        load(sa, ra);
+    }
+    for (int k0 = kb0; k0 < ke; k0 += 32 * DEPTH) {
+#pragma unroll
+      for (int j = 0; j < DEPTH; ++j) {
+        const int kc = k0 + 32 * j;
+        if (kc >= ke) break;
+        const int jn = (j + DEPTH - 1) % DEPTH;
+        const int kn = kc + 32 * (DEPTH - 1);
+        if (kn < ke) {
+          sp[jn][0] = span(kn);
+          sp[jn][1] = span(kn + 16);
+          load(sp[jn], r[jn]);
+        }
+        compute(kc, sp[j], r[j]);
       }
-      compute(k0 + 32, sb, rb);
     }
 
     // partial result of this piece
     float l_tot = sum_across_rows16(l_run);
     l_tot = sum_across_halves(l_tot);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? os / l_tot : 0.f;
     if (row_ok) {
       // Oᵀ element (m = 4*g + i, c) is d = 8*m + c = 32*g + 8*i + c
       if (32 * g < D) {
@@ -472,8 +551,10 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   DecodeParams pp;
   pp.q = static_cast<const __bf16*>(a.q);
-  pp.k = static_cast<const __bf16*>(a.k_cache);
-  pp.v = static_cast<const __bf16*>(a.v_cache);
+  pp.k = static_cast<const char*>(a.k_cache);
+  pp.v = static_cast<const char*>(a.v_cache);
+  pp.ksc = a.k_scale;
+  pp.vsc = a.v_scale;
   pp.cv.table = a.block_table;
   pp.cv.max_blocks = a.max_blocks;
   pp.cv.num_blocks = a.num_blocks;
@@ -504,17 +585,17 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
   const long long blocks = (pp.W + 3) / 4;
   const long long cblocks = ((long long)a.B * a.Hkv * pp.M + 3) / 4;
   if (blocks > 0x7fffffffLL || cblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.d == 128) {
-    hipLaunchKernelGGL(decode_partial_kernel<128>, dim3((int)blocks), dim3(256), 0, s, pp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  auto partial = a.d == 128 ? (a.kv8 ? decode_partial_kernel<128, true>
+                                      : decode_partial_kernel<128, false>)
+                           : (a.kv8 ? decode_partial_kernel<64, true>
+                                    : decode_partial_kernel<64, false>);
+  hipLaunchKernelGGL(partial, dim3((int)blocks), dim3(256), 0, s, pp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.d == 128)
     hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((int)cblocks), dim3(256), 0, s, pp);
-  } else {
-    hipLaunchKernelGGL(decode_partial_kernel<64>, dim3((int)blocks), dim3(256), 0, s, pp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  else
     hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((int)cblocks), dim3(256), 0, s, pp);
-  }
   return hipGetLastError();
 }
 

@@ -43,6 +43,9 @@ struct DecodeArgs {
   float scale;
   int causal;
   int max_seq_len;
+  int kv8 = 0;        // caches hold E4M3 codes with per-K/V-head scales
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
   int workers;        // waves sharing the key space
   float* part_o;      // [(workers + B*Hkv) * M, d]
   float* part_lse;    // [(workers + B*Hkv) * M]
@@ -59,6 +62,9 @@ struct CacheCopyArgs {
   int num_blocks;
   const int32_t* lens;  // append: cache_lens; gather: seq_lens
   int elem_bytes;
+  // append only: the cache holds E4M3 codes of x / scale[kv head]
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
   int B, Hkv, Nnew, d;
   int max_seq_len;
 };
@@ -71,6 +77,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kv_append(const CacheCopyArgs& a, hipStream_t s);
+hipError_t launch_kv_append_fp8(const CacheCopyArgs& a, hipStream_t s);
 hipError_t launch_gather(const CacheCopyArgs& a, hipStream_t s);
 
 }  // namespace attn

@@ -33,6 +33,9 @@ WORKLOADS = {
                             len_lo=1024, len_hi=16384, dtype="bf16"),
     # chunked prefill: a 512-token chunk per sequence appended after a cached
     # prefix, then attending to the whole paged cache
+    # the paged 4-token decode over an E4M3 cache with per-head scales
+    "paged_decode_q4_fp8": dict(seed=1007, kind="decode_paged_fp8", B=32, Hq=32, Hkv=8, Nq=4,
+                                d=128, len_lo=1024, len_hi=16384, dtype="bf16"),
     "chunked_prefill_paged": dict(seed=1006, kind="prefill_paged", B=8, Hq=32, Hkv=8, Nq=512,
                                   d=128, len_lo=1024, len_hi=8192, dtype="bf16"),
 }
@@ -125,6 +128,34 @@ def paged_inputs(seed, B, Hq, Hkv, Nq, d, len_lo, len_hi, spare_blocks=0, dtype=
                 seq_lens=seq.to(torch.int32).to(device), num_blocks=P)
 
 
+def fp8_scales(Hkv, device="cpu"):
+    """Per-K/V-head scales of a synthetic E4M3 cache: head h's codes stand for
+    values of standard deviation about 0.5 + h / Hkv."""
+    return torch.tensor([(6.0 / 448.0) * (0.5 + h / Hkv) for h in range(Hkv)],
+                        dtype=torch.float32, device=device)
+
+
+def paged_inputs_fp8(seed, B, Hq, Hkv, Nq, d, len_lo, len_hi, spare_blocks=0, device="cpu",
+                     cache_lens=None):
+    """``paged_inputs`` with an E4M3 cache: the same lengths, table, new bf16
+    K/V rows and bf16 queries, while the pools hold codes. The codes are
+    standard normal draws times 448/6, clamped to the finite range and cast to
+    float8_e4m3fn, so with ``fp8_scales`` head h's cached values are about
+    N(0, (0.5 + h/Hkv)^2). Adds k_scale, v_scale [Hkv] f32."""
+    inp = paged_inputs(seed, B, Hq, Hkv, Nq, d, len_lo, len_hi, spare_blocks, "bf16", device,
+                       cache_lens)
+    g = _gen(seed + 7919, device)
+    P = inp["num_blocks"]
+    for name in ("k_pool", "v_pool"):
+        x = torch.randn((P, BLOCK, Hkv, d), generator=g, dtype=torch.float32, device=device)
+        x = (x * (448.0 / 6.0)).clamp_(-448.0, 448.0)
+        inp[name] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        del x
+    inp["k_scale"] = fp8_scales(Hkv, device)
+    inp["v_scale"] = fp8_scales(Hkv, device)
+    return inp
+
+
 def poison_unused(inp, value=float("nan")):
     """Fill every pool row that no sequence uses (spare blocks, tail slots past
     seq_len) with ``value``; returns the number of rows touched."""
@@ -152,5 +183,8 @@ def workload_inputs(name, device="cpu"):
     if w["kind"] == "decode_contig":
         return decode_contig_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["Nq"], w["d"],
                                     w["seq_len"], None, w["dtype"], device)
+    if w["kind"] == "decode_paged_fp8":
+        return paged_inputs_fp8(w["seed"], w["B"], w["Hq"], w["Hkv"], w["Nq"], w["d"],
+                                w["len_lo"], w["len_hi"], 0, device)
     return paged_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["Nq"], w["d"], w["len_lo"],
                         w["len_hi"], 0, w["dtype"], device)

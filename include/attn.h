@@ -158,6 +158,26 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       float scale, int causal, int max_seq_len, int num_splits,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_decode_paged over an fp8 K/V cache: the cache holds E4M3 codes (OCP
+ * 8-bit floating point, "fn" variant: bias 7, no infinities, largest 448),
+ * one byte per element, in the same paged or contiguous layouts; element x of
+ * K/V head h stands for decode(code) · scale[h] ("Phase 07 · 12", section
+ * "Paged attention": the fp8 cache option, which halves the bytes decode
+ * reads). The scores are scale · q·k with those values; O and LSE as for
+ * attn_decode_paged.
+ *   k_scale, v_scale : [Hkv] f32 device arrays, finite and > 0
+ *   q, o             : [B, Nq, Hq, d] bf16; everything else as attn_decode_paged
+ *                      (its workspace size applies unchanged)
+ */
+int attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                          const float* k_scale, const float* v_scale,
+                          const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                          const int32_t* seq_lens, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int d,
+                          float scale, int causal, int max_seq_len, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Worker count attn_decode_paged uses for these arguments (num_splits = 0:
  * the default for the current device), or a negative attn_status. */
 int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
@@ -188,6 +208,19 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
               const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
               const int32_t* cache_lens, int dtype, int B, int Hkv, int Nnew, int d,
               int max_seq_len, void* stream);
+
+/*
+ * kv_append into an fp8 (E4M3) cache: k_new, v_new are bf16 [B, Nnew, Hkv, d];
+ * element x of head h is stored as the code nearest to x / scale[h] (one fp32
+ * division; ties to even), with magnitudes past 448 saturating to ±448.
+ * Layouts, positions and the caller's duties as for kv_append; k_scale,
+ * v_scale are [Hkv] f32 device arrays (the ones attn_decode_paged_fp8 reads).
+ */
+int kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const float* k_scale, const float* v_scale,
+                  const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                  const int32_t* cache_lens, int B, int Hkv, int Nnew, int d,
+                  int max_seq_len, void* stream);
 
 /*
  * Gather the first seq_lens[b] logical rows of every sequence out of a paged

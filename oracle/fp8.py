@@ -28,40 +28,47 @@ import numpy as np
 E4M3_MAX = 448.0
 
 
+def _decode_byte(code):
+    """fp64 value of one E4M3 byte, from its three fields."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return np.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+# the value of every byte, once
+_TABLE = np.array([_decode_byte(c) for c in range(256)], dtype=np.float64)
+
+
 def e4m3_decode(codes):
     """fp64 values of E4M3 bytes (any integer array shape)."""
-    c = np.asarray(codes, dtype=np.int64) & 0xFF
-    out = np.empty(c.shape, dtype=np.float64)
-    flat_c = c.reshape(-1)
-    flat_o = out.reshape(-1)
-    for i, code in enumerate(flat_c):
-        sign = -1.0 if code & 0x80 else 1.0
-        e = (code >> 3) & 0xF
-        m = code & 0x7
-        if e == 0xF and m == 0x7:
-            flat_o[i] = np.nan
-        elif e == 0:
-            flat_o[i] = sign * (m / 8.0) * 2.0 ** -6
-        else:
-            flat_o[i] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
-    return out
+    return _TABLE[np.asarray(codes, dtype=np.int64) & 0xFF]
 
 
 # codes 0x00..0x7E (all non-negative finite values), ascending
 _POS_CODES = np.arange(0x7F, dtype=np.int64)
-_POS_VALUES = e4m3_decode(_POS_CODES)
+_POS_VALUES = _TABLE[:0x7F]
 
 
-def _encode_one(v):
-    """Nearest non-negative E4M3 code of a non-negative finite v <= 448."""
-    # distance to every finite value; the nearest wins, ties go to the even code
-    dist = np.abs(_POS_VALUES - v)
-    best = int(np.argmin(dist))
-    ties = np.nonzero(dist == dist[best])[0]
-    if len(ties) > 1:
-        even = [int(t) for t in ties if int(_POS_CODES[t]) % 2 == 0]
-        best = even[0]
-    return int(_POS_CODES[best])
+def _encode_magnitudes(a):
+    """Nearest non-negative E4M3 codes of non-negative finite values <= 448:
+    the entry of the value table at the smallest distance; when the next
+    entry is exactly as close, the even code of the two."""
+    a = np.asarray(a, dtype=np.float64).reshape(-1)
+    out = np.empty(a.shape, dtype=np.int64)
+    for s0 in range(0, a.size, 1 << 16):  # bounded memory for the distance matrix
+        chunk = a[s0:s0 + (1 << 16)]
+        dist = np.abs(_POS_VALUES[None, :] - chunk[:, None])
+        best = np.argmin(dist, axis=1)  # the lower index on a tie
+        nxt = np.minimum(best + 1, len(_POS_VALUES) - 1)
+        tie = (nxt != best) & (dist[np.arange(len(chunk)), nxt] == dist[np.arange(len(chunk)), best])
+        pick = np.where(tie & (_POS_CODES[best] % 2 == 1), nxt, best)
+        out[s0:s0 + len(chunk)] = _POS_CODES[pick]
+    return out
 
 
 def e4m3_encode(values):
@@ -69,18 +76,13 @@ def e4m3_encode(values):
     nearest representable value, ties to even. NaN encodes as 0x7F (with its
     sign bit)."""
     x = np.asarray(values, dtype=np.float32)
-    out = np.empty(x.shape, dtype=np.uint8)
-    flat_x = x.reshape(-1)
-    flat_o = out.reshape(-1)
-    for i, v in enumerate(flat_x):
-        v = float(v)
-        neg = np.signbit(v)
-        if np.isnan(v):
-            flat_o[i] = 0x7F | (0x80 if neg else 0)
-            continue
-        a = min(abs(v), E4M3_MAX)
-        flat_o[i] = _encode_one(a) | (0x80 if neg else 0)
-    return out
+    v = x.astype(np.float64).reshape(-1)
+    neg = np.signbit(v)
+    nan = np.isnan(v)
+    mag = np.minimum(np.abs(np.where(nan, 0.0, v)), E4M3_MAX)
+    code = _encode_magnitudes(mag)
+    code = np.where(nan, 0x7F, code) | np.where(neg, 0x80, 0)
+    return code.astype(np.uint8).reshape(x.shape)
 
 
 def quantize(x, scale):

@@ -199,3 +199,53 @@ def test_prefill_rejects_key_counts_past_32_bit_offsets():
     st = lib.attn_prefill(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 8, 8, 16, (1 << 22) + 1, 128, 0.1, 1,
                           0, None)
     assert st == eta.ATTN_EUNSUPPORTED
+
+
+def _decode_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, bt=None, mb=0, nb=0, sl=FAKE, o=FAKE,
+             lse=None, B=2, Hq=32, Hkv=8, Nq=4, d=128, scale=0.1, causal=1, L=4096, S=0, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return eta.library().attn_decode_paged_fp8(
+        a["q"], a["k"], a["v"], a["ks"], a["vs"], a["bt"], a["mb"], a["nb"], a["sl"], a["o"],
+        a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["d"], a["scale"], a["causal"], a["L"],
+        a["S"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=None), eta.ATTN_EINVAL),
+    (dict(vs=None), eta.ATTN_EINVAL),
+    (dict(ks=P(0x10002)), eta.ATTN_EINVAL),   # misaligned scale array
+    (dict(d=80), eta.ATTN_EUNSUPPORTED),
+    (dict(Nq=17), eta.ATTN_EUNSUPPORTED),     # 4 heads x 17 rows > 64
+    (dict(ws=None), eta.ATTN_EWORKSPACE),
+    (dict(scale=0.0), eta.ATTN_EINVAL),
+])
+def test_decode_fp8_rejects(kw, code):
+    assert _decode_fp8(**kw) == code
+
+
+def _append_fp8(**kw):
+    a = dict(kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=None, mb=0, nb=0, cl=FAKE,
+             B=2, Hkv=8, Nnew=4, d=128, L=4096)
+    a.update(kw)
+    return eta.library().kv_append_fp8(a["kn"], a["vn"], a["kc"], a["vc"], a["ks"], a["vs"],
+                                       a["bt"], a["mb"], a["nb"], a["cl"], a["B"], a["Hkv"],
+                                       a["Nnew"], a["d"], a["L"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=None), eta.ATTN_EINVAL),
+    (dict(vs=P(0x10001)), eta.ATTN_EINVAL),
+    (dict(kc=None), eta.ATTN_EINVAL),
+    (dict(d=96), eta.ATTN_EUNSUPPORTED),
+    (dict(cl=None), eta.ATTN_EINVAL),
+    (dict(bt=FAKE, mb=0), eta.ATTN_EINVAL),
+])
+def test_append_fp8_rejects(kw, code):
+    assert _append_fp8(**kw) == code
+
+
+def test_fp8_entries_with_nothing_to_do():
+    assert _append_fp8(B=0) == eta.ATTN_OK
+    assert _decode_fp8(Nq=0) == eta.ATTN_OK

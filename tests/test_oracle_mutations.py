@@ -98,16 +98,16 @@ FP8 = ("e4m3_decode", "e4m3_encode", "quantize", "dequantize")
 
 FP8_MUTANTS = [
     ("exponent bias 8 (the FNUZ variant)",
-     "flat_o[i] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
-     "flat_o[i] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)",
+     "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)",
+     "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)",
      fp8pins.test_decode_matches_torch_for_every_code),
     ("ties away from zero",
-     "even = [int(t) for t in ties if int(_POS_CODES[t]) % 2 == 0]",
-     "even = [int(t) for t in ties][::-1]",
+     "pick = np.where(tie & (_POS_CODES[best] % 2 == 1), nxt, best)",
+     "pick = np.where(tie, nxt, best)",
      fp8pins.test_closed_forms),
     ("no saturation beyond 448",
-     "a = min(abs(v), E4M3_MAX)",
-     "a = abs(v) if abs(v) <= E4M3_MAX else float('nan')",
+     "mag = np.minimum(np.abs(np.where(nan, 0.0, v)), E4M3_MAX)",
+     "mag = np.abs(np.where(nan, 0.0, v))",
      fp8pins.test_closed_forms),
     ("scale multiplied instead of divided",
      "y = (xf / s).astype(np.float32)",
