@@ -139,7 +139,8 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
  *                 num_splits/Hkv workers; the head's 32-key steps of all
  *                 sequences are laid end to end and cut into that many equal
  *                 ranges, so the split adapts to ragged lengths. 0 picks a
- *                 default for the current device (a few per compute unit).
+ *                 default for the current device: one worker per SIMD (four
+ *                 per compute unit) here, two per SIMD for the fp8 cache.
  *   workspace   : device scratch of at least attn_decode_workspace_bytes()
  *                 bytes for the same arguments, owned by the caller and
  *                 free again once the call's work on `stream` is done. It
@@ -183,8 +184,9 @@ int attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cach
 int attn_decode_num_splits(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
                            int num_splits);
 
-/* Workspace bytes attn_decode_paged needs for these arguments; 0 if they are
- * invalid. */
+/* Workspace bytes attn_decode_paged and attn_decode_paged_fp8 need for these
+ * arguments (the larger of the two when their default worker counts differ);
+ * 0 if they are invalid. */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int max_seq_len,
                                    int num_splits);
 
