@@ -13,7 +13,9 @@ Each stage is timed with HIP events recorded on the stream the library
 launches on; the long-context prefill (N=32768), the chunked prefill against
 the paged cache (8 sequences, 512 new tokens after 1k-8k cached ones), the
 paged 4-token decode over an fp8 (E4M3) cache and the fp32 single-head case
-are timed in their own loops after the steps. FLOPs count visible
+are timed in their own loops after the steps. Last, on the host, the 1000-chat
+serving simulation compares the native block pool (paged cache) with
+contiguous allocation. FLOPs count visible
 (query, key) pairs x 4d; decode bytes count each visible K/V row once.
 Prints ONE JSON line.
 """
@@ -61,6 +63,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--long-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chat-sim", action="store_true",
+                    help="skip the host-side 1000-chat block-pool simulation")
     ap.add_argument("--stage", default=None,
                     choices=["prefill_4k", "prefill_32k", "splitkv_decode_32k", "paged_decode_q4",
                              "chunked_prefill_paged", "paged_decode_q4_fp8", "copy_1gib"],
@@ -403,6 +407,22 @@ def main():
                 "traffic": traffic, "traffic_unit": "bytes per launch (HBM read + write)",
                 "kernel": "prefill_bf16_kernel<128, causal, slabs>",
                 "per_launch": f"{flops2:.6g} FLOP (visible pairs x 4d) per launch"}
+
+    if not args.no_chat_sim:
+        from exact_tiled_attention_flashattention_amd import chat_sim
+
+        print("[bench] 1000-chat block-pool simulation (host)", file=sys.stderr, flush=True)
+        cfg = inputs.CHAT_SIM
+        prompts, outputs = inputs.chat_lengths(**cfg)
+        t_sim = time.perf_counter()
+        sims = chat_sim.compare(prompts, outputs, cfg["capacity_tokens"], cfg["max_new_tokens"])
+        result_workloads["paged_pool_chat_sim"] = {
+            "chats": cfg["chats"], "capacity_tokens": cfg["capacity_tokens"],
+            "lengths": f"prompt U[{cfg['prompt_lo']},{cfg['prompt_hi']}], "
+                       f"output U[{cfg['output_lo']},{cfg['output_hi']}]",
+            "host_seconds": round(time.perf_counter() - t_sim, 2),
+            "schemes": {r["scheme"]: {k: (round(v, 4) if isinstance(v, float) else v)
+                                      for k, v in r.items() if k != "scheme"} for r in sims}}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
     attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, ...) -> (o, lse)
     kv_append(k_new, v_new, k_cache, v_cache, cache_lens, block_table=None, ...)
     attn_gather_paged(cache, seq_lens, block_table, max_seq_len)     -> out
+    BlockPool(num_blocks).grow(table_row, cur_len, new_len) / .release(table_row, len)
 """
 
 import ctypes
@@ -28,6 +29,7 @@ ATTN_EINVAL = -1
 ATTN_EUNSUPPORTED = -2
 ATTN_EWORKSPACE = -3
 ATTN_EHIP = -4
+ATTN_ENOSPACE = -5
 ATTN_F32 = 0
 ATTN_BF16 = 1
 BLOCK_TOKENS = 16
@@ -72,6 +74,16 @@ def _load():
     lib.kv_append.restype = I
     lib.attn_gather_paged.argtypes = [P, P, I, I, P, P, I, I, I, I, I, P]
     lib.attn_gather_paged.restype = I
+    lib.attn_block_pool_bytes.argtypes = [I]
+    lib.attn_block_pool_bytes.restype = SZ
+    lib.attn_block_pool_init.argtypes = [P, SZ, I]
+    lib.attn_block_pool_init.restype = I
+    lib.attn_block_pool_free_count.argtypes = [P]
+    lib.attn_block_pool_free_count.restype = I
+    lib.attn_block_pool_grow.argtypes = [P, P, I, I, I]
+    lib.attn_block_pool_grow.restype = I
+    lib.attn_block_pool_release.argtypes = [P, P, I, I]
+    lib.attn_block_pool_release.restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -356,7 +368,59 @@ def attn_gather_paged(cache, seq_lens, block_table=None, max_seq_len=None, out=N
     return out
 
 
+class BlockPool:
+    """Host-side pool of a paged cache's physical 16-token blocks (the C ABI's
+    attn_block_pool_*; the state sits in a buffer this object owns). Table rows
+    are host int32 numpy arrays (-1 = no block); copy the table to the device
+    before a kernel reads it."""
+
+    def __init__(self, num_blocks):
+        lib = _load()
+        n = int(lib.attn_block_pool_bytes(int(num_blocks)))
+        if n == 0:
+            raise ValueError("num_blocks must be >= 0")
+        self._buf = (ctypes.c_int32 * ((n + 3) // 4))()
+        self.num_blocks = int(num_blocks)
+        _check(lib.attn_block_pool_init(ctypes.addressof(self._buf), n, self.num_blocks),
+               "attn_block_pool_init")
+
+    def _addr(self):
+        return ctypes.addressof(self._buf)
+
+    @staticmethod
+    def _row(table_row):
+        import numpy as np
+
+        if not isinstance(table_row, np.ndarray) or table_row.dtype != np.int32 or \
+                table_row.ndim != 1 or not table_row.flags["C_CONTIGUOUS"] or \
+                not table_row.flags["WRITEABLE"]:
+            raise TypeError("a table row is a writeable contiguous 1-D int32 numpy array")
+        return table_row.ctypes.data, table_row.shape[0]
+
+    def free_count(self):
+        st = _load().attn_block_pool_free_count(self._addr())
+        _check(min(st, 0), "attn_block_pool_free_count")
+        return st
+
+    def grow(self, table_row, cur_len, new_len):
+        """Blocks for positions [cur_len, new_len); False (nothing changed) when the
+        pool has too few free blocks."""
+        ptr, mb = self._row(table_row)
+        st = _load().attn_block_pool_grow(self._addr(), ptr, mb, int(cur_len), int(new_len))
+        if st == ATTN_ENOSPACE:
+            return False
+        _check(st, "attn_block_pool_grow")
+        return True
+
+    def release(self, table_row, length):
+        """Free-on-finish: the sequence's ceil(length/16) blocks go back to the pool."""
+        ptr, mb = self._row(table_row)
+        _check(_load().attn_block_pool_release(self._addr(), ptr, mb, int(length)),
+               "attn_block_pool_release")
+
+
 __all__ = [
+    "BlockPool",
     "attn_prefill",
     "attn_prefill_paged",
     "attn_decode_paged_fp8",

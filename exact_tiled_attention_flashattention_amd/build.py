@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "kv_cache.hip"]
+SOURCES = ["attn_api.cpp", "block_pool.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip",
+           "kv_cache.hip"]
 ARCH = "gfx950"
 
 

@@ -118,6 +118,7 @@ const char* attn_strerror(int status) {
     case ATTN_EUNSUPPORTED: return "unsupported dtype, head dim or group size";
     case ATTN_EWORKSPACE: return "workspace missing or too small";
     case ATTN_EHIP: return "HIP runtime error at launch";
+    case ATTN_ENOSPACE: return "not enough free blocks in the pool";
     default: return "unknown status";
   }
 }

@@ -31,14 +31,30 @@ WORKLOADS = {
                                d=128, seq_len=32768, dtype="bf16"),
     "paged_decode_q4": dict(seed=1005, kind="decode_paged", B=32, Hq=32, Hkv=8, Nq=4, d=128,
                             len_lo=1024, len_hi=16384, dtype="bf16"),
-    # chunked prefill: a 512-token chunk per sequence appended after a cached
-    # prefix, then attending to the whole paged cache
     # the paged 4-token decode over an E4M3 cache with per-head scales
     "paged_decode_q4_fp8": dict(seed=1007, kind="decode_paged_fp8", B=32, Hq=32, Hkv=8, Nq=4,
                                 d=128, len_lo=1024, len_hi=16384, dtype="bf16"),
+    # chunked prefill: a 512-token chunk per sequence appended after a cached
+    # prefix, then attending to the whole paged cache
     "chunked_prefill_paged": dict(seed=1006, kind="prefill_paged", B=8, Hq=32, Hkv=8, Nq=512,
                                   d=128, len_lo=1024, len_hi=8192, dtype="bf16"),
 }
+
+# 1000 chat completions served from a cache of 65536 token positions (8 GiB
+# for a 32-layer model with 8 K/V heads of dim 128 in bf16: 128 KiB per
+# token); prompt and output lengths uniform on [32, 2048]; a contiguous
+# allocator that cannot know the output length reserves 2048 new tokens
+CHAT_SIM = dict(seed=1008, chats=1000, prompt_lo=32, prompt_hi=2048, output_lo=32,
+                output_hi=2048, capacity_tokens=65536, max_new_tokens=2048)
+
+
+def chat_lengths(seed, chats, prompt_lo, prompt_hi, output_lo, output_hi, **_):
+    """Prompt and output lengths of `chats` chat completions, each uniform on
+    its inclusive integer range, drawn prompts first. Returns two int lists."""
+    g = _gen(seed, "cpu")
+    p = torch.randint(prompt_lo, prompt_hi + 1, (chats,), generator=g)
+    r = torch.randint(output_lo, output_hi + 1, (chats,), generator=g)
+    return [int(x) for x in p], [int(x) for x in r]
 
 
 def torch_dtype(name):

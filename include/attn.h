@@ -51,7 +51,8 @@ typedef enum attn_status {
   ATTN_EINVAL = -1,       /* bad argument: null pointer, negative size, Hq % Hkv != 0 */
   ATTN_EUNSUPPORTED = -2, /* valid but not built: dtype, head dim, group size */
   ATTN_EWORKSPACE = -3,   /* workspace NULL or smaller than attn_decode_workspace_bytes() */
-  ATTN_EHIP = -4          /* the HIP runtime reported an error at launch */
+  ATTN_EHIP = -4,         /* the HIP runtime reported an error at launch */
+  ATTN_ENOSPACE = -5      /* block pool: not enough free blocks (nothing changed) */
 } attn_status;
 
 typedef enum attn_dtype { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -234,6 +235,42 @@ int kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_c
 int attn_gather_paged(const void* cache, const int32_t* block_table, int max_blocks_per_seq,
                       int num_blocks, const int32_t* seq_lens, void* out, int dtype, int B,
                       int Hkv, int d, int max_seq_len, void* stream);
+
+/*
+ * Block pool of a paged cache ("Phase 07 · 12", sections "Paged attention"
+ * and "Exercises": fixed 16-token blocks behind a page table, returned to the
+ * pool as soon as a sequence finishes). HOST-side bookkeeping only: it decides
+ * which physical block of a [num_blocks, 16, Hkv, d] pool backs each logical
+ * block of a sequence, writing block ids into a HOST copy of that sequence's
+ * block-table row (int32, -1 = no block); the caller copies the table to the
+ * device before the kernels read it. The pool's state lives in `pool`, a
+ * caller-owned host buffer of attn_block_pool_bytes(num_blocks) bytes, 4-byte
+ * aligned; the library allocates nothing. A fresh pool hands out blocks
+ * 0, 1, 2, ... in order; released blocks are reused last-freed first. Not
+ * thread-safe: calls on one pool must be serialised by the caller.
+ */
+size_t attn_block_pool_bytes(int num_blocks);
+
+/* Set up a pool of num_blocks free blocks in `pool` (pool_bytes at least
+ * attn_block_pool_bytes(num_blocks), else ATTN_EWORKSPACE). */
+int attn_block_pool_init(void* pool, size_t pool_bytes, int num_blocks);
+
+/* Free blocks left, or ATTN_EINVAL for a buffer that holds no pool. */
+int attn_block_pool_free_count(const void* pool);
+
+/* Give a sequence growing from cur_len to new_len tokens storage: the logical
+ * blocks [ceil(cur_len/16), ceil(new_len/16)) of table_row (which must be -1
+ * there, else ATTN_EINVAL) receive fresh blocks. All or nothing: with too few
+ * free blocks it returns ATTN_ENOSPACE and changes nothing.
+ * ceil(new_len/16) must not exceed max_blocks_per_seq. */
+int attn_block_pool_grow(void* pool, int32_t* table_row, int max_blocks_per_seq, int cur_len,
+                         int new_len);
+
+/* Free-on-finish: return the ceil(len/16) blocks of a finished sequence to
+ * the pool and set those entries of table_row to -1. Every entry must name a
+ * block this pool handed out and that is not yet released (each at most once),
+ * else ATTN_EINVAL and nothing changes. */
+int attn_block_pool_release(void* pool, int32_t* table_row, int max_blocks_per_seq, int len);
 
 /* A static string naming a status code. */
 const char* attn_strerror(int status);
