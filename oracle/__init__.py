@@ -28,6 +28,12 @@ exists at once in fp64 and the softmax sees the whole row. Sources:
   "Cachebedarf berechnen" (M_KV = 2·L·B·T·Hkv·d·e) and "Der wichtige
   Maskenfehler beim Cache" (the causal mask must carry a position offset when
   the query is shorter than the keys).
+* backward.py: the gradients dQ, dK, dV of the same definition (the chain
+  rule through S, softmax and P V; "Phase 07 · 12", section "tiling trick",
+  notes that the backward pass recomputes forward values instead of storing
+  them).
+* pool.py: the paged cache's block pool as a plain set, and the chat-serving
+  schedule of "Phase 07 · 12", section "Exercises" (item 3).
 * fp8.py: the E4M3 encoding of a quantised K/V cache with per-head scales
   (the fp8 cache option of "Phase 07 · 12", section "Paged attention"; the
   encoding is the OCP 8-bit format, a reading stated in that module).
@@ -48,6 +54,7 @@ from .paged import gather_paged, gather_contiguous, kv_append_ref
 from .online import online_attention_rows
 from .counts import kv_cache_bytes, visible_pairs, naive_vs_cached_kv_states
 from .fp8 import E4M3_MAX, e4m3_decode, e4m3_encode, quantize, dequantize
+from .backward import attention_backward_rows, prefill_backward
 
 __all__ = [
     "NEG_INF",
@@ -67,4 +74,6 @@ __all__ = [
     "e4m3_encode",
     "quantize",
     "dequantize",
+    "attention_backward_rows",
+    "prefill_backward",
 ]
