@@ -9,6 +9,7 @@ raises.
 
 Entry points (same names as the C ABI):
     attn_prefill(q, k, v, scale=None, causal=False, q_offset=0)      -> (o, lse)
+    attn_prefill_backward(q, k, v, o, lse, dout, ...)                -> (dq, dk, dv)
     attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, ...) -> (o, lse)
     kv_append(k_new, v_new, k_cache, v_cache, cache_lens, block_table=None, ...)
     attn_gather_paged(cache, seq_lens, block_table, max_seq_len)     -> out
@@ -74,6 +75,11 @@ def _load():
     lib.kv_append.restype = I
     lib.attn_gather_paged.argtypes = [P, P, I, I, P, P, I, I, I, I, I, P]
     lib.attn_gather_paged.restype = I
+    lib.attn_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
+                                          I, P, SZ, P]
+    lib.attn_prefill_backward.restype = I
+    lib.attn_prefill_backward_workspace_bytes.argtypes = [I, I, I]
+    lib.attn_prefill_backward_workspace_bytes.restype = SZ
     lib.attn_block_pool_bytes.argtypes = [I]
     lib.attn_block_pool_bytes.restype = SZ
     lib.attn_block_pool_init.argtypes = [P, SZ, I]
@@ -149,6 +155,48 @@ def attn_prefill(q, k, v, scale=None, causal=False, q_offset=0, out=None, lse=No
                           _stream(q.device))
     _check(st, "attn_prefill")
     return out, lse
+
+
+def attn_prefill_backward(q, k, v, o, lse, dout, scale=None, causal=False, q_offset=0, dq=None,
+                          dk=None, dv=None, workspace=None):
+    """Backward of attn_prefill (bf16). q, o, dout [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d];
+    lse [B,Hq,Nq] f32 from the forward -> dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d]."""
+    lib = _load()
+    _need_gpu(q, k, v, o, lse, dout)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    for t in (k, v, o, dout):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, o, dout must share one dtype")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, Nq):
+        raise ValueError("lse must be float32 [B, Hq, Nq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    need = int(lib.attn_prefill_backward_workspace_bytes(B, Hq, Nq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need_gpu(dq, dk, dv, workspace)
+    st = lib.attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q), B, Hq, Hkv, Nq,
+                                   Nk, d, float(scale), int(bool(causal)), int(q_offset),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(q.device))
+    _check(st, "attn_prefill_backward")
+    return dq, dk, dv
+
+
+def attn_prefill_backward_workspace_bytes(B, Hq, Nq):
+    return int(_load().attn_prefill_backward_workspace_bytes(B, Hq, Nq))
 
 
 def _check_cache_args(q, k_cache, v_cache, seq_lens, block_table):
@@ -421,6 +469,8 @@ class BlockPool:
 
 __all__ = [
     "BlockPool",
+    "attn_prefill_backward",
+    "attn_prefill_backward_workspace_bytes",
     "attn_prefill",
     "attn_prefill_paged",
     "attn_decode_paged_fp8",

@@ -21,7 +21,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libattn.so")
 
 SOURCES = ["attn_api.cpp", "block_pool.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip",
-           "kv_cache.hip"]
+           "kv_cache.hip", "backward_bf16.hip"]
 ARCH = "gfx950"
 
 

@@ -146,6 +146,43 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
                                       : attn::launch_prefill_f32(a, s));
 }
 
+size_t attn_prefill_backward_workspace_bytes(int B, int Hq, int Nq) {
+  if (B < 0 || Hq <= 0 || Nq < 0) return 0;
+  const size_t n = (size_t)B * (size_t)Hq * (size_t)Nq * sizeof(float);
+  return n < 256 ? 256 : (n + 255) / 256 * 256;
+}
+
+int attn_prefill_backward(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                          int causal, int q_offset, void* workspace, size_t workspace_bytes_given,
+                          void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0) return ATTN_EINVAL;
+  if (Hq % Hkv != 0) return ATTN_EINVAL;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
+  if (q_offset > (1 << 30) || q_offset < -(1 << 30)) return ATTN_EINVAL;
+  if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  if (!head_dim_ok(d)) return ATTN_EUNSUPPORTED;
+  if ((long long)Nk * d * 2 > 0x7fffffffLL || (long long)Nq * d * 2 > 0x7fffffffLL)
+    return ATTN_EUNSUPPORTED;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return ATTN_OK;
+  if (Nq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
+                 dq == nullptr))
+    return ATTN_EINVAL;
+  if (Nk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return ATTN_EINVAL;
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(o) ||
+      misaligned16(dout) || misaligned16(dq) || misaligned16(dk) || misaligned16(dv) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return ATTN_EINVAL;
+  if (workspace == nullptr || misaligned16(workspace) ||
+      workspace_bytes_given < attn_prefill_backward_workspace_bytes(B, Hq, Nq))
+    return ATTN_EWORKSPACE;
+  attn::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
+                       B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, q_offset};
+  return status_of(attn::launch_backward_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
                        const int32_t* seq_lens, void* o, float* lse, int dtype, int B, int Hq,

@@ -1,0 +1,548 @@
+// Backward pass of causal / non-causal GQA prefill attention, bf16 inputs,
+// fp32 accumulation, gfx950 MFMA.
+//
+// Method ("Phase 07 · 12: KV cache, Flash Attention and inference
+// optimisation", section "tiling trick": the backward pass recomputes the
+// forward's intermediate values instead of storing them). With the forward's
+// per-row log-sum-exp L, a tile's probabilities are recomputed exactly as
+// P = exp(scale·q·k − L) without any running max, and the chain rule through
+// O = P V, the row softmax and S = scale·Q Kᵀ gives, per tile,
+//     dV += Pᵀ dO,  dP = dO Vᵀ,  dS = P ∘ (dP − D),  dQ += scale·dS K,
+//     dK += scale·dSᵀ Q,        with D_i = dO_i · O_i (one number per row).
+// Neither S, P nor dS ever reaches device memory.
+//
+// Two kernels, so that no output needs atomics:
+//   * bwd_dq_kernel: one workgroup per (query block, K/V head, head group),
+//     the forward's decomposition. A wave owns 32 query rows and streams the
+//     K/V tiles through LDS; it computes Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ with Qᵀ,
+//     dOᵀ in registers (one query row per lane), so L and D are per-lane
+//     constants, and dQᵀ += Kᵀ·dSᵀ with Kᵀ read through the transposing LDS
+//     read. It also writes D to the workspace.
+//   * bwd_dkdv_kernel: one workgroup per (128-key block, K/V head). A wave
+//     owns 32 keys, holds its K and V rows in registers and streams the
+//     Q / dO tiles of every query head of the group through LDS; it computes
+//     S = Q·Kᵀ and dP = dO·Vᵀ (one key per lane), then dVᵀ += dOᵀ·P and
+//     dKᵀ += Qᵀ·dS with dOᵀ, Qᵀ read through the transposing LDS read. The sum
+//     over the G query heads of the group happens in the accumulators.
+// Tiles are 64 rows of D bf16, loaded straight from global memory into an
+// XOR-swizzled LDS layout in which both the row reads (MFMA A operand) and
+// the transposing reads are conflict-free, double-buffered with one barrier
+// per tile.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kTile = 64;                  // rows per streamed tile
+constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, 32-bit dword data
+
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  const float* lse;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  float* drow;  // [B, Hq, Nq] workspace: D_i = dO_i · O_i
+  int B, Hq, Hkv, Nq, Nk;
+  int G;       // Hq / Hkv
+  int hw;      // heads per dQ workgroup (1, 2 or 4)
+  int pw;      // 32-row slices per head in a dQ workgroup (4 / hw)
+  int n_qblk;  // dQ query blocks of 32 * pw rows
+  int n_hgrp;  // dQ workgroups per K/V head and query block (G / hw)
+  int n_kblk;  // dK/dV key blocks of 128 keys
+  float c;     // scale * log2(e)
+  float scale;
+  int q_offset;
+};
+
+// Tile rows live in LDS unpadded (D*2 bytes per row) with the 16-byte chunks
+// of row r permuted by chunk ^ swz(r): 16 consecutive rows read at one chunk
+// and the transposing reads (4 rows x 4 chunks per 32 lanes) both hit
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return (row >> 1) & 7;
+}
+
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int elem) {
+  return row * (D * 2) + ((((elem >> 3) ^ swz<D>(row))) << 4) + ((elem & 7) << 1);
+}
+
+// Loads of one 64-row tile (rows of 2*D bytes, contiguous from `tile`, of
+// which `bytes` are valid) into LDS `dst`: each of the 4 waves issues NI
+// 1 KiB direct-to-LDS loads; lane l of load i writes LDS bytes
+// (wave*NI + i)*1024 + 16*l, the physical chunk that the swizzle assigns to
+// the logical chunk the lane fetches. The resource starts at the tile and
+// ends after its valid bytes, and every offset is a per-lane (range-checked)
+// one, so rows past the end arrive as zeros.
+template <int D>
+__device__ __forceinline__ void load_tile(const void* tile, long long bytes, char* dst, int wave,
+                                          int lane) {
+  constexpr int NI = kTile * D * 2 / (kWaves * 1024);
+  constexpr int kXorStep = (D == 128) ? 16 : 64;
+  static_assert((D == 128 && NI == 4) || (D == 64 && NI == 2),
+                "the per-load chunk flip assumes 4 (d=128) or 2 (d=64) loads per wave");
+  const int range = (int)(bytes < 0 ? 0 : (bytes > kTile * D * 2 ? kTile * D * 2 : bytes));
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(tile), 0, range, kBufferFlags);
+  int lb = (D == 128) ? ((lane >> 4) * (D * 2)) | (16 * ((lane & 15) ^ (4 * (lane >> 4))))
+                      : ((lane >> 3) * (D * 2)) | (16 * ((lane & 7) ^ (lane >> 4)));
+  asm volatile("" : "+v"(lb));
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(dst + (wave * NI + i) * 1024),
+                                             16, (lb ^ (kXorStep * i)) + (wave * NI + i) * 1024,
+                                             0, 0, 0);
+}
+
+// Transposing read of a 32(d) x 16(row) A operand from a row-major tile: rows
+// r0, r0 + 8 (r0 already holds the lane's row within its group), columns col..
+template <int D>
+__device__ __forceinline__ bf16x8_t read_tr(const char* tile, int r0, int col) {
+  const i16x4_t lo =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4_t*)(tile + lds_off<D>(r0, col)));
+  const i16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4_t*)(tile + lds_off<D>(r0 + 8, col)));
+  const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+  const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+  const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
+  return __builtin_bit_cast(bf16x8_t, a4);
+}
+
+// base-2 log-sum-exp of a row from the forward's natural-log LSE; a row that
+// saw no key (LSE = -inf) gets +inf, so every recomputed P of it is 0
+__device__ __forceinline__ float lse2_of(float lse) {
+  return lse == neg_inf() ? __builtin_inff() : lse * kLog2e;
+}
+
+// ============================================================================
+// dQ (and D)
+// ============================================================================
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TILE = kTile * D * 2;
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int per_q = p.B * p.Hkv * p.n_hgrp;
+  const int qrank = blockIdx.x / per_q;
+  int rest = blockIdx.x - qrank * per_q;
+  const int hg = rest % p.n_hgrp;
+  rest /= p.n_hgrp;
+  const int kvh = rest % p.Hkv;
+  const int b = rest / p.Hkv;
+  const int qblk = CAUSAL ? (p.n_qblk - 1 - qrank) : qrank;
+  const int head_local = wave % p.hw;
+  const int sub = wave / p.hw;
+  const int hq = kvh * p.G + hg * p.hw + head_local;
+  const int q0 = qblk * 32 * p.pw;
+  const int my_q = q0 + sub * 32 + l32;
+  const bool row_ok = my_q < p.Nq;
+
+  int kend = p.Nk;
+  if (CAUSAL) {
+    const long long lim = (long long)min(q0 + 32 * p.pw, p.Nq) - 1 + p.q_offset + 1;
+    if (lim < kend) kend = (int)(lim < 0 ? 0 : lim);
+  }
+  const int ntiles = (kend + kTile - 1) / kTile;
+  long long mask_from = p.Nk;
+  if (CAUSAL) {
+    const long long first = (long long)q0 + p.q_offset + 1;
+    if (first < mask_from) mask_from = first;
+  }
+  long long lim64 = CAUSAL ? (long long)my_q + p.q_offset : (long long)p.Nk - 1;
+  if (lim64 > (long long)p.Nk - 1) lim64 = (long long)p.Nk - 1;
+  if (lim64 < -1) lim64 = -1;
+  const int lim = (int)lim64;
+
+  // Qᵀ and dOᵀ as B operands: lane holds row my_q, d = 16*dc + 8*g + j; and
+  // D = dO·O of the row (the lane's half of d, then across the halves)
+  const long long row_off = (((long long)b * p.Hq + hq) * p.Nq + my_q) * D + 8 * g;
+  bf16x8_t qf[NDC], df[NDC];
+  float dsum = 0.f;
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) {
+    if (row_ok) {
+      qf[dc] = *reinterpret_cast<const bf16x8_t*>(p.q + row_off + 16 * dc);
+      df[dc] = *reinterpret_cast<const bf16x8_t*>(p.dout + row_off + 16 * dc);
+      const bf16x8_t of = *reinterpret_cast<const bf16x8_t*>(p.o + row_off + 16 * dc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dsum += (float)df[dc][j] * (float)of[j];
+    } else {
+      qf[dc] = bf16x8_t{};
+      df[dc] = bf16x8_t{};
+    }
+  }
+  const float drow = sum_across_halves(dsum);
+  const long long ridx = ((long long)b * p.Hq + hq) * p.Nq + my_q;
+  const float lse2 = row_ok ? lse2_of(p.lse[ridx]) : __builtin_inff();
+  if (row_ok && g == 0) p.drow[ridx] = drow;
+
+  const long long kv_base = ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
+  const long long kv_bytes = (long long)p.Nk * D * 2;
+
+  f32x16_t acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
+
+  const int grp = lane >> 4;
+  const int src = lane & 15;
+  const int tr_row = src >> 2;
+  const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
+
+  auto tile_step = [&](int it, const char* kl, const char* vl) __attribute__((always_inline)) {
+    const int k0 = it * kTile;
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+      dp[kb] = f32x16_t{};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
+            kl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dc], s[kb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
+            vl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[dc], dp[kb], 0, 0, 0);
+      }
+    }
+    const bool masked = k0 + kTile > mask_from || k0 + kTile > p.Nk;
+    // dSᵀ = Pᵀ ∘ (dPᵀ − D), packed to bf16 in Sᵀ register order
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float e[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 2 * j + h;
+          float x = s[kb][i];
+          if (masked) {
+            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key > lim) x = neg_inf();
+          }
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -lse2));
+          e[h] = pr * (dp[kb][i] - drow);
+        }
+        pk[kb][j] = pack_bf16x2(e[0], e[1]);
+      }
+    // dQᵀ += Kᵀ dSᵀ, 16 keys per MFMA; Kᵀ through the transposing LDS read
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4_t w4 = {pk[kb][4 * hf], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2],
+                            pk[kb][4 * hf + 3]};
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, w4);
+        const int r0 = kb * 32 + 16 * hf + 4 * g + tr_row;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kl, r0, 32 * db + tr_col),
+                                                            bop, acc[db], 0, 0, 0);
+      }
+  };
+
+  if (ntiles > 0) {
+    load_tile<D>(p.k + kv_base, kv_bytes, kb0, wave, lane);
+    load_tile<D>(p.v + kv_base, kv_bytes, vb0, wave, lane);
+    for (int it = 0; it < ntiles; ++it) {
+      char* kc = (it & 1) ? kb1 : kb0;
+      char* vc = (it & 1) ? vb1 : vb0;
+      char* kn = (it & 1) ? kb0 : kb1;
+      char* vn = (it & 1) ? vb0 : vb1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it has landed
+      __syncthreads();                     // ... for every wave; tile it-1's buffers are free
+      if (it + 1 < ntiles) {
+        const long long t0 = (long long)(it + 1) * kTile * D;
+        load_tile<D>(p.k + kv_base + t0, kv_bytes - 2 * t0, kn, wave, lane);
+        load_tile<D>(p.v + kv_base + t0, kv_bytes - 2 * t0, vn, wave, lane);
+      }
+      tile_step(it, kc, vc);
+    }
+  }
+
+  if (row_ok) {
+    __bf16* op = p.dq + ((long long)b * p.Hq + hq) * p.Nq * D + (long long)my_q * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        f32x4_t v4 = {acc[db][4 * ii] * p.scale, acc[db][4 * ii + 1] * p.scale,
+                      acc[db][4 * ii + 2] * p.scale, acc[db][4 * ii + 3] * p.scale};
+        *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * ii + 4 * g) =
+            __builtin_convertvector(v4, bf16x4_t);
+      }
+  }
+}
+
+// ============================================================================
+// dK, dV
+// ============================================================================
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NDC = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TILE = kTile * D * 2;
+  __shared__ __attribute__((aligned(1024))) char qb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char qb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char ob0[TILE];  // dO tiles
+  __shared__ __attribute__((aligned(1024))) char ob1[TILE];
+  __shared__ __attribute__((aligned(16))) float ld0[2 * kTile];  // LSE then D of the tile rows
+  __shared__ __attribute__((aligned(16))) float ld1[2 * kTile];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  // key blocks in increasing order: under a causal mask the first blocks
+  // see the most query rows, so the longest workgroups start first
+  const int per_k = p.B * p.Hkv;
+  const int kblk = blockIdx.x / per_k;
+  const int rest = blockIdx.x - kblk * per_k;
+  const int kvh = rest % p.Hkv;
+  const int b = rest / p.Hkv;
+  const int k0 = kblk * (kWaves * 32);        // first key of the workgroup
+  const int kw0 = k0 + wave * 32;              // first key of the wave
+  const int my_key = kw0 + l32;
+
+  // K and V rows of the wave's keys as B operands: lane holds key my_key,
+  // d = 16*dc + 8*g + j
+  const long long kv_base = ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
+  bf16x8_t kf[NDC], vf[NDC];
+#pragma unroll
+  for (int dc = 0; dc < NDC; ++dc) {
+    if (my_key < p.Nk) {
+      kf[dc] = *reinterpret_cast<const bf16x8_t*>(p.k + kv_base + (long long)my_key * D + 16 * dc +
+                                                   8 * g);
+      vf[dc] = *reinterpret_cast<const bf16x8_t*>(p.v + kv_base + (long long)my_key * D + 16 * dc +
+                                                   8 * g);
+    } else {
+      kf[dc] = bf16x8_t{};
+      vf[dc] = bf16x8_t{};
+    }
+  }
+
+  // query tiles that can see any key of the block: rows i >= k0 - q_offset
+  int qt_lo = 0;
+  if (CAUSAL) {
+    const long long first_row = (long long)k0 - p.q_offset;
+    qt_lo = first_row <= 0 ? 0 : (int)min(first_row / kTile, (long long)0x3fffffff);
+  }
+  const int n_qt = (p.Nq + kTile - 1) / kTile;
+  const int per_head = n_qt > qt_lo ? n_qt - qt_lo : 0;
+  const int nsteps = per_head * p.G;
+
+  f32x16_t acck[NDB], accv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acck[db] = f32x16_t{};
+    accv[db] = f32x16_t{};
+  }
+
+  const int grp = lane >> 4;
+  const int src = lane & 15;
+  const int tr_row = src >> 2;
+  const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
+
+  // step s: query head kvh*G + s / per_head, tile qt_lo + s % per_head
+  auto issue = [&](int s, char* qdst, char* odst, float* ldst) __attribute__((always_inline)) {
+    const int hq = kvh * p.G + s / per_head;
+    const int qt = qt_lo + s % per_head;
+    const long long hbase = ((long long)b * p.Hq + hq) * (long long)p.Nq;
+    const long long r0 = (long long)qt * kTile;   // first row of the tile
+    const long long left = (long long)p.Nq - r0;  // rows of the head from there on
+    load_tile<D>(p.q + (hbase + r0) * D, left * D * 2, qdst, wave, lane);
+    load_tile<D>(p.dout + (hbase + r0) * D, left * D * 2, odst, wave, lane);
+    if (wave < 2) {  // wave 0: LSE of the 64 rows, wave 1: D (rows past Nq read 0)
+      const float* srcp = (wave == 0 ? p.lse : p.drow) + hbase + r0;
+      const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(srcp), 0, (int)(left >= kTile ? kTile * 4 : left * 4), kBufferFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (ATTN_LDS void*)(ldst + wave * kTile), 4,
+                                               4 * lane, 0, 0, 0);
+    }
+  };
+
+  auto step = [&](int s, const char* ql, const char* ol, const float* ll)
+      __attribute__((always_inline)) {
+    const int qt = qt_lo + s % per_head;
+    const int qrow0 = qt * kTile;
+    // under a causal mask, pairs are hidden only where a row precedes a key
+    const bool masked = CAUSAL && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(
+            ql + lds_off<D>(qb * 32 + l32, 16 * dc + 8 * g));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[dc], sc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(
+            ol + lds_off<D>(qb * 32 + l32, 16 * dc + 8 * g));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[dc], dp, 0, 0, 0);
+      }
+      // accumulator i holds row qb*32 + 8*(i/4) + 4*g + i%4 of the tile
+      uint32_t pp[8], pd[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(ll + qb * 32 + 8 * m + 4 * g);
+        const f32x4_t d4 =
+            *reinterpret_cast<const f32x4_t*>(ll + kTile + qb * 32 + 8 * m + 4 * g);
+        float pv[4], dv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * m + r;
+          float x = sc[i];
+          if (masked) {
+            const int row = qrow0 + qb * 32 + 8 * m + 4 * g + r;
+            if ((long long)my_key > (long long)row + p.q_offset) x = neg_inf();
+          }
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -lse2_of(l4[r])));
+          pv[r] = pr;
+          dv[r] = pr * (dp[i] - d4[r]);
+        }
+        pp[2 * m] = pack_bf16x2(pv[0], pv[1]);
+        pp[2 * m + 1] = pack_bf16x2(pv[2], pv[3]);
+        pd[2 * m] = pack_bf16x2(dv[0], dv[1]);
+        pd[2 * m + 1] = pack_bf16x2(dv[2], dv[3]);
+      }
+      // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS, 16 rows per MFMA
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4_t wp = {pp[4 * hf], pp[4 * hf + 1], pp[4 * hf + 2], pp[4 * hf + 3]};
+        const u32x4_t wd = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
+        const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, wp);
+        const bf16x8_t bd = __builtin_bit_cast(bf16x8_t, wd);
+        const int r0 = qb * 32 + 16 * hf + 4 * g + tr_row;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ol, r0, 32 * db + tr_col),
+                                                             bp, accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ql, r0, 32 * db + tr_col),
+                                                             bd, acck[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    issue(0, qb0, ob0, ld0);
+    for (int s = 0; s < nsteps; ++s) {
+      char* qc = (s & 1) ? qb1 : qb0;
+      char* oc = (s & 1) ? ob1 : ob0;
+      float* lc = (s & 1) ? ld1 : ld0;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step s's tiles have landed
+      __syncthreads();                     // ... for every wave; step s-1's buffers are free
+      if (s + 1 < nsteps) issue(s + 1, (s & 1) ? qb0 : qb1, (s & 1) ? ob0 : ob1,
+                                (s & 1) ? ld0 : ld1);
+      step(s, qc, oc, lc);
+    }
+  }
+
+  if (my_key < p.Nk) {
+    const long long off = kv_base + (long long)my_key * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        f32x4_t k4 = {acck[db][4 * ii] * p.scale, acck[db][4 * ii + 1] * p.scale,
+                      acck[db][4 * ii + 2] * p.scale, acck[db][4 * ii + 3] * p.scale};
+        f32x4_t v4 = {accv[db][4 * ii], accv[db][4 * ii + 1], accv[db][4 * ii + 2],
+                      accv[db][4 * ii + 3]};
+        *reinterpret_cast<bf16x4_t*>(p.dk + off + 32 * db + 8 * ii + 4 * g) =
+            __builtin_convertvector(k4, bf16x4_t);
+        *reinterpret_cast<bf16x4_t*>(p.dv + off + 32 * db + 8 * ii + 4 * g) =
+            __builtin_convertvector(v4, bf16x4_t);
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const BwdParams& bp, bool causal, int nq_blocks, int nk_blocks,
+                    hipStream_t s) {
+  if (nq_blocks > 0) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(nq_blocks), dim3(kWaves * 64), 0, s, bp);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(nq_blocks), dim3(kWaves * 64), 0, s, bp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nk_blocks > 0) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(nk_blocks), dim3(kWaves * 64), 0, s, bp);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(nk_blocks), dim3(kWaves * 64), 0, s,
+                         bp);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t s) {
+  BwdParams bp;
+  bp.q = static_cast<const __bf16*>(a.q);
+  bp.k = static_cast<const __bf16*>(a.k);
+  bp.v = static_cast<const __bf16*>(a.v);
+  bp.o = static_cast<const __bf16*>(a.o);
+  bp.dout = static_cast<const __bf16*>(a.dout);
+  bp.lse = a.lse;
+  bp.dq = static_cast<__bf16*>(a.dq);
+  bp.dk = static_cast<__bf16*>(a.dk);
+  bp.dv = static_cast<__bf16*>(a.dv);
+  bp.drow = a.drow;
+  bp.B = a.B;
+  bp.Hq = a.Hq;
+  bp.Hkv = a.Hkv;
+  bp.Nq = a.Nq;
+  bp.Nk = a.Nk;
+  bp.G = a.Hq / a.Hkv;
+  bp.hw = (bp.G % 4 == 0) ? 4 : ((bp.G % 2 == 0) ? 2 : 1);
+  bp.pw = kWaves / bp.hw;
+  bp.n_qblk = (a.Nq + 32 * bp.pw - 1) / (32 * bp.pw);
+  bp.n_hgrp = bp.G / bp.hw;
+  bp.n_kblk = (a.Nk + kWaves * 32 - 1) / (kWaves * 32);
+  bp.c = a.scale * kLog2e;
+  bp.scale = a.scale;
+  bp.q_offset = a.q_offset;
+  const long long nq = (long long)bp.n_qblk * a.B * a.Hkv * bp.n_hgrp;
+  const long long nk = (long long)bp.n_kblk * a.B * a.Hkv;
+  if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (a.d == 128) return launch_d<128>(bp, a.causal != 0, (int)nq, (int)nk, s);
+  return launch_d<64>(bp, a.causal != 0, (int)nq, (int)nk, s);
+}
+
+}  // namespace attn

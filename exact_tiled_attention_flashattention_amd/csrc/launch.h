@@ -69,12 +69,30 @@ struct CacheCopyArgs {
   int max_seq_len;
 };
 
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* drow;  // workspace: [B, Hq, Nq] f32
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  int q_offset;
+};
+
 // Compute units of the current device (cached per device; 256 when none can
 // be queried).
 int device_compute_units();
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_kv_append(const CacheCopyArgs& a, hipStream_t s);
 hipError_t launch_kv_append_fp8(const CacheCopyArgs& a, hipStream_t s);

@@ -38,6 +38,9 @@ WORKLOADS = {
     # prefix, then attending to the whole paged cache
     "chunked_prefill_paged": dict(seed=1006, kind="prefill_paged", B=8, Hq=32, Hkv=8, Nq=512,
                                   d=128, len_lo=1024, len_hi=8192, dtype="bf16"),
+    # the backward pass of the 4k causal GQA prefill (q, k, v, then dO)
+    "causal_gqa_backward_4k": dict(seed=1009, kind="backward", B=1, Hq=32, Hkv=8, N=4096,
+                                   d=128, dtype="bf16", causal=True),
 }
 
 # 1000 chat completions served from a cache of 65536 token positions (8 GiB
@@ -70,6 +73,18 @@ def _gen(seed, device):
 def _normal(shape, g, dtype, device):
     x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
     return x if dtype == torch.float32 else x.to(dtype)
+
+
+def backward_inputs(seed, B, Hq, Hkv, Nq, Nk, d, dtype="bf16", device="cpu"):
+    """q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d], dout [B,Hq,Nq,d] (the gradient of
+    the loss with respect to O), drawn in that order from one generator."""
+    g = _gen(seed, device)
+    dt = torch_dtype(dtype)
+    q = _normal((B, Hq, Nq, d), g, dt, device)
+    k = _normal((B, Hkv, Nk, d), g, dt, device)
+    v = _normal((B, Hkv, Nk, d), g, dt, device)
+    dout = _normal((B, Hq, Nq, d), g, dt, device)
+    return q, k, v, dout
 
 
 def prefill_inputs(seed, B, Hq, Hkv, Nq, Nk, d, dtype="bf16", device="cpu"):
@@ -196,6 +211,9 @@ def workload_inputs(name, device="cpu"):
     if w["kind"] == "prefill":
         return prefill_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["N"], w["d"],
                               w["dtype"], device)
+    if w["kind"] == "backward":
+        return backward_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["N"], w["d"],
+                               w["dtype"], device)
     if w["kind"] == "decode_contig":
         return decode_contig_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["Nq"], w["d"],
                                     w["seq_len"], None, w["dtype"], device)

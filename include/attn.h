@@ -192,6 +192,35 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int ma
                                    int num_splits);
 
 /*
+ * Backward pass of attn_prefill ("Phase 07 · 12", section "tiling trick": the
+ * backward pass recomputes the forward's intermediate values from the inputs
+ * instead of storing them). Given dout = dLoss/dO it returns
+ *     dq = scale · dS K,  dk = scale · dSᵀ Q,  dv = Pᵀ dout,
+ * with P the forward's probabilities, dS = P ∘ (dout Vᵀ − D) and
+ * D_i = dout_i · o_i; under GQA, dk and dv of a K/V head are summed over the
+ * Hq/Hkv query heads that read it. P is recomputed tile by tile from q, k and
+ * the forward's lse (exp(scale·q·k − lse)); no score matrix is stored.
+ *   q, o, dout, dq : [B, Hq, Nq, d] bf16   (o and lse exactly as attn_prefill
+ *   k, v, dk, dv   : [B, Hkv, Nk, d] bf16   returned them for these inputs)
+ *   lse            : [B, Hq, Nq] f32
+ *   causal, q_offset, scale : as for attn_prefill
+ *   workspace      : device scratch of at least
+ *                    attn_prefill_backward_workspace_bytes(B, Hq, Nq) bytes
+ *                    (it receives D); calls that share one must be ordered on
+ *                    one stream. It needs no clearing.
+ * Every element of dq, dk and dv is written (keys no row sees get 0).
+ * Supported: dtype ATTN_BF16 (fp32 accumulation), d in {64, 128}.
+ */
+int attn_prefill_backward(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                          int causal, int q_offset, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes attn_prefill_backward needs; 0 if the sizes are invalid. */
+size_t attn_prefill_backward_workspace_bytes(int B, int Hq, int Nq);
+
+/*
  * Append Nnew new K/V rows per sequence to the cache (the decode step grows
  * the cache by concatenation: "大模型面试笔记——Attention篇" §4; "Phase 07 ·
  * 12", "Build it, step 1").

@@ -249,3 +249,38 @@ def test_append_fp8_rejects(kw, code):
 def test_fp8_entries_with_nothing_to_do():
     assert _append_fp8(B=0) == eta.ATTN_OK
     assert _decode_fp8(Nq=0) == eta.ATTN_OK
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             dtype=1, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=128, scale=0.1, causal=1, q_offset=0,
+             ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    lib = eta.library()
+    return lib.attn_prefill_backward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                                     a["dk"], a["dv"], a["dtype"], a["B"], a["Hq"], a["Hkv"],
+                                     a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                     a["q_offset"], a["ws"], a["ws_bytes"], None)
+
+
+def test_backward_rejects_bad_arguments():
+    assert _bwd(Hq=3, Hkv=2) == eta.ATTN_EINVAL
+    assert _bwd(scale=0.0) == eta.ATTN_EINVAL
+    assert _bwd(scale=float("nan")) == eta.ATTN_EINVAL
+    assert _bwd(dtype=0) == eta.ATTN_EUNSUPPORTED      # fp32 backward is not built
+    assert _bwd(d=96) == eta.ATTN_EUNSUPPORTED
+    assert _bwd(q=None) == eta.ATTN_EINVAL
+    assert _bwd(dk=None) == eta.ATTN_EINVAL
+    assert _bwd(lse=None) == eta.ATTN_EINVAL
+    assert _bwd(q=P(0x10008)) == eta.ATTN_EINVAL          # not 16-byte aligned
+    assert _bwd(ws=None) == eta.ATTN_EWORKSPACE
+    assert _bwd(ws_bytes=16) == eta.ATTN_EWORKSPACE
+    assert _bwd(B=-1) == eta.ATTN_EINVAL
+    assert _bwd(B=0) == eta.ATTN_OK                       # nothing to do, nothing enqueued
+
+
+def test_backward_workspace_size():
+    lib = eta.library()
+    assert lib.attn_prefill_backward_workspace_bytes(1, 32, 4096) == 32 * 4096 * 4
+    assert lib.attn_prefill_backward_workspace_bytes(1, 1, 1) == 256
+    assert lib.attn_prefill_backward_workspace_bytes(-1, 1, 1) == 0

@@ -159,6 +159,20 @@ def test_gqa_sums_over_the_group():
     assert np.abs(dV - mV.reshape(B, Hkv, 3, N, d).sum(axis=2)).max() <= 1e-13
 
 
+def test_magnitudes_bound_the_gradients():
+    # each magnitude is a sum of the absolute values of the gradient's terms,
+    # so it bounds the gradient; it is zero exactly where every term is
+    rng = np.random.default_rng(12)
+    q = _rand(rng, 1, 4, 33, 8)
+    k = _rand(rng, 1, 2, 40, 8)
+    v = _rand(rng, 1, 2, 40, 8)
+    do = _rand(rng, 1, 4, 33, 8)
+    dQ, dK, dV, (mq, mk, mv) = ob.prefill_backward(q, k, v, do, 0.4, True, 0, magnitudes=True)
+    for g, m in ((dQ, mq), (dK, mk), (dV, mv)):
+        assert (np.abs(g) <= m * (1 + 1e-12) + 1e-300).all()
+    assert (mk[:, :, 33:] == 0).all() and (mv[:, :, 33:] == 0).all()  # keys no row sees
+
+
 def test_kv_head_sample_matches_full():
     rng = np.random.default_rng(9)
     q = _rand(rng, 2, 4, 9, 4)
@@ -196,7 +210,7 @@ BWD_MUTANTS = [
     ("dV from the scores", "dv += P.T @ dout[r0:r1]", "dv += E.T @ dout[r0:r1]"),
     ("mask off by one", "S[np.arange(n)[None, :] > pos[r0:r1, None]] = NEG_INF",
      "S[np.arange(n)[None, :] >= pos[r0:r1, None]] = NEG_INF"),
-    ("GQA group overwritten", "dK[b, g] += bk", "dK[b, g] = bk"),
+    ("GQA group overwritten", "dK[b, g] += res[1]", "dK[b, g] = res[1]"),
 ]
 
 
