@@ -9,9 +9,13 @@ seeded workload with inputs already resident in HBM:
   * kv_append of 4 new tokens + paged 4-token decode, B=32, 16-token blocks,
     cached lengths uniform in [1024, 16384],
   * split-KV decode of 1 token against 16 contiguous 32768-token caches.
-Each stage is timed with HIP events recorded on the stream the library
+Before the W warmup steps the step runs untimed for --settle-seconds (0.3 s)
+so that the GPU clocks have reached their loaded level: the first ~30 ms of
+work on an idle MI355X run about 10% slower. Each stage is timed with HIP
+events recorded on the stream the library
 launches on; the long-context prefill (N=32768), the chunked prefill against
 the paged cache (8 sequences, 512 new tokens after 1k-8k cached ones), the
+backward pass of the 4k prefill, the
 paged 4-token decode over an fp8 (E4M3) cache and the fp32 single-head case
 are timed in their own loops after the steps. Last, on the host, the 1000-chat
 serving simulation compares the native block pool (paged cache) with
@@ -62,12 +66,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--long-steps", type=int, default=5)
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="run the step untimed for this long before the warmup steps, so the "
+                         "GPU clocks reach their loaded level (the first ~30 ms of work run "
+                         "about 10%% slower)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chat-sim", action="store_true",
                     help="skip the host-side 1000-chat block-pool simulation")
     ap.add_argument("--stage", default=None,
                     choices=["prefill_4k", "prefill_32k", "splitkv_decode_32k", "paged_decode_q4",
-                             "chunked_prefill_paged", "paged_decode_q4_fp8", "copy_1gib"],
+                             "chunked_prefill_paged", "paged_decode_q4_fp8", "backward_4k",
+                             "copy_1gib"],
                     help="run only this stage --steps times and exit (for profiler runs); "
                          "copy_1gib is a plain 1 GiB device copy used to calibrate HBM counters")
     return ap.parse_args()
@@ -86,6 +95,14 @@ def run_stage(args, torch, eta, inputs, dev):
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         fn = lambda: eta.attn_prefill(q, k, v, causal=True, out=o, lse=lse)  # noqa: E731
+    elif name == "backward_4k":
+        q, k, v, do = inputs.workload_inputs("causal_gqa_backward_4k", dev)
+        o, lse = eta.attn_prefill(q, k, v, causal=True)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(eta.attn_prefill_backward_workspace_bytes(*q.shape[:3]),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: eta.attn_prefill_backward(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk,  # noqa
+                                               dv=dv, workspace=ws)
     elif name == "chunked_prefill_paged":
         p = inputs.workload_inputs(name, dev)
         eta.kv_append(p["k_new"], p["v_new"], p["k_pool"], p["v_pool"], p["cache_lens"],
@@ -271,11 +288,19 @@ def main():
               ("paged_decode_q4", decode5), ("splitkv_decode_32k", decode4)]
     timer = StageTimer(torch, stream, [n for n, _ in stages])
 
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for n, fn in stages:
+            timer.run(n, fn, record=False)
+        torch.cuda.synchronize()
+        settle += 1
     for _ in range(args.warmup):
         for n, fn in stages:
             timer.run(n, fn, record=False)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] clock settle {settle} steps, warmup {args.warmup} steps; timing {args.steps} "
+          f"steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         for n, fn in stages:
@@ -354,6 +379,34 @@ def main():
         "frac_of_peak": round(flops6 / (ms6 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops": flops6}
     del p6, o6, l6
+    torch.cuda.empty_cache()
+    # the backward pass of the 4k causal GQA prefill (dQ kernel, then dK/dV kernel)
+    w8 = inputs.WORKLOADS["causal_gqa_backward_4k"]
+    q8, k8, v8, do8 = inputs.workload_inputs("causal_gqa_backward_4k", dev)
+    o8, l8 = eta.attn_prefill(q8, k8, v8, causal=True)
+    dq8, dk8, dv8 = torch.empty_like(q8), torch.empty_like(k8), torch.empty_like(v8)
+    ws8 = torch.empty(eta.attn_prefill_backward_workspace_bytes(w8["B"], w8["Hq"], w8["N"]),
+                      dtype=torch.uint8, device=dev)
+
+    def bwd8():
+        eta.attn_prefill_backward(q8, k8, v8, o8, l8, do8, causal=True, dq=dq8, dk=dk8, dv=dv8,
+                                  workspace=ws8)
+
+    t8 = StageTimer(torch, stream, ["p"])
+    for _ in range(3):
+        bwd8()
+    for _ in range(20):
+        t8.run("p", bwd8)
+    torch.cuda.synchronize()
+    ms8 = t8.mean_ms("p")
+    flops8 = 2.5 * prefill_flops(w8["B"], w8["Hq"], w8["N"], w8["d"])
+    result_workloads["causal_gqa_backward_4k"] = {
+        "ms": round(ms8, 5), "TFLOP/s": round(flops8 / (ms8 * 1e-3) / 1e12, 2),
+        "frac_of_peak": round(flops8 / (ms8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flops": flops8,
+        "flop_convention": "five products per visible pair (QK^T, dO V^T, P^T dO, dS K, dS^T Q),"
+                           " 2.5x the forward's; the kernels recompute QK^T and dO V^T once more"}
+    del q8, k8, v8, do8, o8, l8, dq8, dk8, dv8, ws8
     torch.cuda.empty_cache()
     # the paged 4-token decode over an E4M3 cache (one byte per element)
     w7 = inputs.WORKLOADS["paged_decode_q4_fp8"]
