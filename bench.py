@@ -99,8 +99,9 @@ def run_stage(args, torch, eta, inputs, dev):
         q, k, v, do = inputs.workload_inputs("causal_gqa_backward_4k", dev)
         o, lse = eta.attn_prefill(q, k, v, causal=True)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(eta.attn_prefill_backward_workspace_bytes(*q.shape[:3]),
-                         dtype=torch.uint8, device=dev)
+        ws = torch.empty(eta.attn_prefill_backward_workspace_bytes(
+            q.shape[0], q.shape[1], k.shape[1], q.shape[2], k.shape[2], q.shape[3], True),
+            dtype=torch.uint8, device=dev)
         fn = lambda: eta.attn_prefill_backward(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk,  # noqa
                                                dv=dv, workspace=ws)
     elif name == "chunked_prefill_paged":
@@ -385,7 +386,8 @@ def main():
     q8, k8, v8, do8 = inputs.workload_inputs("causal_gqa_backward_4k", dev)
     o8, l8 = eta.attn_prefill(q8, k8, v8, causal=True)
     dq8, dk8, dv8 = torch.empty_like(q8), torch.empty_like(k8), torch.empty_like(v8)
-    ws8 = torch.empty(eta.attn_prefill_backward_workspace_bytes(w8["B"], w8["Hq"], w8["N"]),
+    ws8 = torch.empty(eta.attn_prefill_backward_workspace_bytes(w8["B"], w8["Hq"], w8["Hkv"],
+                                                                w8["N"], w8["N"], w8["d"], True),
                       dtype=torch.uint8, device=dev)
 
     def bwd8():

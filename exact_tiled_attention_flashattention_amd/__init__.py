@@ -78,7 +78,7 @@ def _load():
     lib.attn_prefill_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I,
                                           I, P, SZ, P]
     lib.attn_prefill_backward.restype = I
-    lib.attn_prefill_backward_workspace_bytes.argtypes = [I, I, I]
+    lib.attn_prefill_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.attn_prefill_backward_workspace_bytes.restype = SZ
     lib.attn_block_pool_bytes.argtypes = [I]
     lib.attn_block_pool_bytes.restype = SZ
@@ -182,7 +182,8 @@ def attn_prefill_backward(q, k, v, o, lse, dout, scale=None, causal=False, q_off
         dk = torch.empty_like(k)
     if dv is None:
         dv = torch.empty_like(v)
-    need = int(lib.attn_prefill_backward_workspace_bytes(B, Hq, Nq))
+    need = int(lib.attn_prefill_backward_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                                                         int(q_offset)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _need_gpu(dq, dk, dv, workspace)
@@ -195,8 +196,9 @@ def attn_prefill_backward(q, k, v, o, lse, dout, scale=None, causal=False, q_off
     return dq, dk, dv
 
 
-def attn_prefill_backward_workspace_bytes(B, Hq, Nq):
-    return int(_load().attn_prefill_backward_workspace_bytes(B, Hq, Nq))
+def attn_prefill_backward_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal=False, q_offset=0):
+    return int(_load().attn_prefill_backward_workspace_bytes(B, Hq, Hkv, Nq, Nk, d,
+                                                             int(bool(causal)), int(q_offset)))
 
 
 def _check_cache_args(q, k_cache, v_cache, seq_lens, block_table):

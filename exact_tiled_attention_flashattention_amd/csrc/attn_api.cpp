@@ -146,10 +146,17 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
                                       : attn::launch_prefill_f32(a, s));
 }
 
-size_t attn_prefill_backward_workspace_bytes(int B, int Hq, int Nq) {
-  if (B < 0 || Hq <= 0 || Nq < 0) return 0;
-  const size_t n = (size_t)B * (size_t)Hq * (size_t)Nq * sizeof(float);
-  return n < 256 ? 256 : (n + 255) / 256 * 256;
+static bool backward_sizes_ok(int B, int Hq, int Hkv, int Nq, int Nk, int d, int q_offset) {
+  return B >= 0 && Hq > 0 && Hkv > 0 && Nq >= 0 && Nk >= 0 && Hq % Hkv == 0 && head_dim_ok(d) &&
+         q_offset <= (1 << 30) && q_offset >= -(1 << 30);
+}
+
+size_t attn_prefill_backward_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                             int causal, int q_offset) {
+  if (!backward_sizes_ok(B, Hq, Hkv, Nq, Nk, d, q_offset)) return 0;
+  return attn::plan_backward(B, Hq, Hkv, Nq, Nk, d, causal != 0, q_offset,
+                             attn::device_compute_units())
+      .bytes;
 }
 
 int attn_prefill_backward(const void* q, const void* k, const void* v, const void* o,
@@ -175,11 +182,14 @@ int attn_prefill_backward(const void* q, const void* k, const void* v, const voi
       misaligned16(dout) || misaligned16(dq) || misaligned16(dk) || misaligned16(dv) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
     return ATTN_EINVAL;
-  if (workspace == nullptr || misaligned16(workspace) ||
-      workspace_bytes_given < attn_prefill_backward_workspace_bytes(B, Hq, Nq))
+  const attn::BackwardPlan pl = attn::plan_backward(B, Hq, Hkv, Nq, Nk, d, causal != 0, q_offset,
+                                                    attn::device_compute_units());
+  if (workspace == nullptr || misaligned16(workspace) || workspace_bytes_given < pl.bytes)
     return ATTN_EWORKSPACE;
   attn::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
                        B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, q_offset};
+  a.nsplit = pl.nsplit;
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_offset);
   return status_of(attn::launch_backward_bf16(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -18,12 +18,16 @@
 //     dOᵀ in registers (one query row per lane), so L and D are per-lane
 //     constants, and dQᵀ += Kᵀ·dSᵀ with Kᵀ read through the transposing LDS
 //     read. It also writes D to the workspace.
-//   * bwd_dkdv_kernel: one workgroup per (128-key block, K/V head). A wave
-//     owns 32 keys, holds its K and V rows in registers and streams the
-//     Q / dO tiles of every query head of the group through LDS; it computes
-//     S = Q·Kᵀ and dP = dO·Vᵀ (one key per lane), then dVᵀ += dOᵀ·P and
-//     dKᵀ += Qᵀ·dS with dOᵀ, Qᵀ read through the transposing LDS read. The sum
-//     over the G query heads of the group happens in the accumulators.
+//   * bwd_dkdv_kernel: one workgroup per (128-key block, K/V head, share of
+//     the group's query heads). A wave owns 32 keys, holds its K and V rows
+//     in registers and streams the Q / dO tiles of its query heads through
+//     LDS; it computes S = Q·Kᵀ and dP = dO·Vᵀ (one key per lane), then
+//     dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with dOᵀ, Qᵀ read through the transposing
+//     LDS read. The sum over those heads happens in the accumulators. When
+//     the group is shared by several workgroups (so that, under a causal
+//     mask, no workgroup holds far more than its share of the work), each
+//     writes fp32 partial sums and bwd_reduce_kernel adds them in a fixed
+//     order: the result does not depend on timing.
 // Tiles are 64 rows of D bf16, loaded straight from global memory into an
 // XOR-swizzled LDS layout in which both the row reads (MFMA A operand) and
 // the transposing reads are conflict-free, double-buffered with one barrier
@@ -56,6 +60,8 @@ struct BwdParams {
   int n_qblk;  // dQ query blocks of 32 * pw rows
   int n_hgrp;  // dQ workgroups per K/V head and query block (G / hw)
   int n_kblk;  // dK/dV key blocks of 128 keys
+  int nsplit;  // dK/dV workgroups per (key block, K/V head): each takes G / nsplit query heads
+  float* part;  // nsplit > 1: fp32 partial dK then dV, [nsplit][B][Hkv][Nk][D] each
   float c;     // scale * log2(e)
   float scale;
   int q_offset;
@@ -325,11 +331,14 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   // key blocks in increasing order: under a causal mask the first blocks
   // see the most query rows, so the longest workgroups start first
-  const int per_k = p.B * p.Hkv;
+  const int per_k = p.B * p.Hkv * p.nsplit;
   const int kblk = blockIdx.x / per_k;
-  const int rest = blockIdx.x - kblk * per_k;
+  int rest = blockIdx.x - kblk * per_k;
+  const int split = rest % p.nsplit;
+  rest /= p.nsplit;
   const int kvh = rest % p.Hkv;
   const int b = rest / p.Hkv;
+  const int gs = p.G / p.nsplit;  // query heads of this workgroup
   const int k0 = kblk * (kWaves * 32);        // first key of the workgroup
   const int kw0 = k0 + wave * 32;              // first key of the wave
   const int my_key = kw0 + l32;
@@ -359,7 +368,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   }
   const int n_qt = (p.Nq + kTile - 1) / kTile;
   const int per_head = n_qt > qt_lo ? n_qt - qt_lo : 0;
-  const int nsteps = per_head * p.G;
+  const int nsteps = per_head * gs;
 
   f32x16_t acck[NDB], accv[NDB];
 #pragma unroll
@@ -373,9 +382,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int tr_row = src >> 2;
   const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
 
-  // step s: query head kvh*G + s / per_head, tile qt_lo + s % per_head
+  // step s: query head kvh*G + split*gs + s / per_head, tile qt_lo + s % per_head
   auto issue = [&](int s, char* qdst, char* odst, float* ldst) __attribute__((always_inline)) {
-    const int hq = kvh * p.G + s / per_head;
+    const int hq = kvh * p.G + split * gs + s / per_head;
     const int qt = qt_lo + s % per_head;
     const long long hbase = ((long long)b * p.Hq + hq) * (long long)p.Nq;
     const long long r0 = (long long)qt * kTile;   // first row of the tile
@@ -472,6 +481,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   if (my_key < p.Nk) {
     const long long off = kv_base + (long long)my_key * D;
+    // nsplit > 1: this workgroup's share, fp32, at [split][b][kvh][key][d]
+    const long long plane = (long long)p.B * p.Hkv * p.Nk * D;
+    float* pk = p.part + split * plane + off;
+    float* pv = p.part + (p.nsplit + split) * plane + off;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -480,17 +493,44 @@ void bwd_dkdv_kernel(BwdParams p) {
                       acck[db][4 * ii + 2] * p.scale, acck[db][4 * ii + 3] * p.scale};
         f32x4_t v4 = {accv[db][4 * ii], accv[db][4 * ii + 1], accv[db][4 * ii + 2],
                       accv[db][4 * ii + 3]};
-        *reinterpret_cast<bf16x4_t*>(p.dk + off + 32 * db + 8 * ii + 4 * g) =
-            __builtin_convertvector(k4, bf16x4_t);
-        *reinterpret_cast<bf16x4_t*>(p.dv + off + 32 * db + 8 * ii + 4 * g) =
-            __builtin_convertvector(v4, bf16x4_t);
+        const int e = 32 * db + 8 * ii + 4 * g;
+        if (p.nsplit == 1) {
+          *reinterpret_cast<bf16x4_t*>(p.dk + off + e) = __builtin_convertvector(k4, bf16x4_t);
+          *reinterpret_cast<bf16x4_t*>(p.dv + off + e) = __builtin_convertvector(v4, bf16x4_t);
+        } else {
+          *reinterpret_cast<f32x4_t*>(pk + e) = k4;
+          *reinterpret_cast<f32x4_t*>(pv + e) = v4;
+        }
       }
   }
+}
+
+// dK, dV = the sums of the nsplit partial sums, added in split order; one
+// thread per 8 elements.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const long long plane = n8 * 8;  // elements of dK (and of dV)
+  const long long e = i * 8;
+  f32x4_t k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+  for (int sp = 0; sp < p.nsplit; ++sp) {
+    const float* a = p.part + sp * plane + e;
+    const float* c = p.part + (p.nsplit + sp) * plane + e;
+    k0 += *reinterpret_cast<const f32x4_t*>(a);
+    k1 += *reinterpret_cast<const f32x4_t*>(a + 4);
+    v0 += *reinterpret_cast<const f32x4_t*>(c);
+    v1 += *reinterpret_cast<const f32x4_t*>(c + 4);
+  }
+  *reinterpret_cast<bf16x4_t*>(p.dk + e) = __builtin_convertvector(k0, bf16x4_t);
+  *reinterpret_cast<bf16x4_t*>(p.dk + e + 4) = __builtin_convertvector(k1, bf16x4_t);
+  *reinterpret_cast<bf16x4_t*>(p.dv + e) = __builtin_convertvector(v0, bf16x4_t);
+  *reinterpret_cast<bf16x4_t*>(p.dv + e + 4) = __builtin_convertvector(v1, bf16x4_t);
 }
 
 template <int D>
 hipError_t launch_d(const BwdParams& bp, bool causal, int nq_blocks, int nk_blocks,
                     hipStream_t s) {
+  const long long n8 = (long long)bp.B * bp.Hkv * bp.Nk * D / 8;
   if (nq_blocks > 0) {
     if (causal)
       hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(nq_blocks), dim3(kWaves * 64), 0, s, bp);
@@ -505,12 +545,56 @@ hipError_t launch_d(const BwdParams& bp, bool causal, int nq_blocks, int nk_bloc
     else
       hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(nk_blocks), dim3(kWaves * 64), 0, s,
                          bp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || bp.nsplit == 1) return e;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, bp,
+                       n8);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
 }  // namespace
+
+BackwardPlan plan_backward(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                           int q_offset, int compute_units) {
+  BackwardPlan pl;
+  const int G = Hq / Hkv;
+  const long long n_kblk = (Nk + kWaves * 32 - 1) / (kWaves * 32);
+  const long long n_qt = (Nq + kTile - 1) / kTile;
+  // query tiles each key block streams per query head, as the kernel counts them
+  long long total = 0, longest = 0;
+  for (long long kb = 0; kb < n_kblk; ++kb) {
+    long long lo = 0;
+    if (causal) {
+      const long long first_row = kb * kWaves * 32 - q_offset;
+      lo = first_row <= 0 ? 0 : first_row / kTile;
+    }
+    const long long st = n_qt > lo ? n_qt - lo : 0;
+    total += st;
+    longest = st > longest ? st : longest;
+  }
+  total *= (long long)G * B * Hkv;
+  // one dK/dV workgroup per compute unit at a time: split the group's query
+  // heads over the fewest workgroups that keep the longest one within the
+  // average load of a compute unit
+  const long long slots = compute_units > 0 ? compute_units : 1;
+  pl.nsplit = G;
+  for (int sp = 1; sp <= G; ++sp) {
+    if (G % sp) continue;
+    if (longest * (G / sp) * slots <= total) {
+      pl.nsplit = sp;
+      break;
+    }
+  }
+  const size_t drow = (size_t)B * Hq * Nq * sizeof(float);
+  pl.part_offset = (drow + 255) / 256 * 256;
+  if (pl.part_offset == 0) pl.part_offset = 256;
+  const size_t part = pl.nsplit > 1 ? 2ull * pl.nsplit * B * Hkv * (size_t)Nk * d * sizeof(float)
+                                    : 0;
+  pl.bytes = pl.part_offset + part;
+  return pl;
+}
 
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t s) {
   BwdParams bp;
@@ -535,11 +619,13 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t s) {
   bp.n_qblk = (a.Nq + 32 * bp.pw - 1) / (32 * bp.pw);
   bp.n_hgrp = bp.G / bp.hw;
   bp.n_kblk = (a.Nk + kWaves * 32 - 1) / (kWaves * 32);
+  bp.nsplit = a.nsplit;
+  bp.part = a.part;
   bp.c = a.scale * kLog2e;
   bp.scale = a.scale;
   bp.q_offset = a.q_offset;
   const long long nq = (long long)bp.n_qblk * a.B * a.Hkv * bp.n_hgrp;
-  const long long nk = (long long)bp.n_kblk * a.B * a.Hkv;
+  const long long nk = (long long)bp.n_kblk * a.B * a.Hkv * bp.nsplit;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.d == 128) return launch_d<128>(bp, a.causal != 0, (int)nq, (int)nk, s);
   return launch_d<64>(bp, a.causal != 0, (int)nq, (int)nk, s);

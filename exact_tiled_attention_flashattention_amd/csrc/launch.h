@@ -84,7 +84,19 @@ struct BackwardArgs {
   float scale;
   int causal;
   int q_offset;
+  int nsplit = 1;        // dK/dV workgroups per (key block, K/V head)
+  float* part = nullptr;  // nsplit > 1: workspace for the fp32 partial sums
 };
+
+// How the backward splits its dK/dV work and lays out its workspace (D, then
+// the partial sums when nsplit > 1).
+struct BackwardPlan {
+  int nsplit = 1;
+  size_t part_offset = 256;
+  size_t bytes = 256;
+};
+BackwardPlan plan_backward(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                           int q_offset, int compute_units);
 
 // Compute units of the current device (cached per device; 256 when none can
 // be queried).

@@ -205,8 +205,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int ma
  *   lse            : [B, Hq, Nq] f32
  *   causal, q_offset, scale : as for attn_prefill
  *   workspace      : device scratch of at least
- *                    attn_prefill_backward_workspace_bytes(B, Hq, Nq) bytes
- *                    (it receives D); calls that share one must be ordered on
+ *                    attn_prefill_backward_workspace_bytes() bytes for the
+ *                    same sizes (it receives D and, when the dK/dV work of a
+ *                    group is shared by several workgroups, their fp32
+ *                    partial sums); calls that share one must be ordered on
  *                    one stream. It needs no clearing.
  * Every element of dq, dk and dv is written (keys no row sees get 0).
  * Supported: dtype ATTN_BF16 (fp32 accumulation), d in {64, 128}.
@@ -217,8 +219,10 @@ int attn_prefill_backward(const void* q, const void* k, const void* v, const voi
                           int causal, int q_offset, void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* Workspace bytes attn_prefill_backward needs; 0 if the sizes are invalid. */
-size_t attn_prefill_backward_workspace_bytes(int B, int Hq, int Nq);
+/* Workspace bytes attn_prefill_backward needs for these arguments on the
+ * current device; 0 if they are invalid. */
+size_t attn_prefill_backward_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                             int causal, int q_offset);
 
 /*
  * Append Nnew new K/V rows per sequence to the cache (the decode step grows

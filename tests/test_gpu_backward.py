@@ -70,6 +70,7 @@ def _run(dev, seed, B, Hq, Hkv, Nq, Nk, d, causal, q_offset, kv_heads=None):
     (1, 4, 1, 70, 50, 128, True, -20),     # rows 0..19 see no key: their dq is 0
     (2, 2, 2, 33, 257, 128, False, 0),
     (1, 6, 2, 190, 190, 64, True, 0),      # G = 3: two heads per workgroup slot
+    (1, 8, 2, 64, 16384, 128, False, 0),   # enough key blocks that each group stays whole
 ])
 def test_backward_matches_oracle(B, Hq, Hkv, Nq, Nk, d, causal, off):
     dev = need_gpu()
