@@ -76,7 +76,7 @@ def parse():
     ap.add_argument("--stage", default=None,
                     choices=["prefill_4k", "prefill_32k", "splitkv_decode_32k", "paged_decode_q4",
                              "chunked_prefill_paged", "paged_decode_q4_fp8", "backward_4k",
-                             "copy_1gib"],
+                             "single_head_f32", "copy_1gib"],
                     help="run only this stage --steps times and exit (for profiler runs); "
                          "copy_1gib is a plain 1 GiB device copy used to calibrate HBM counters")
     return ap.parse_args()
@@ -95,6 +95,11 @@ def run_stage(args, torch, eta, inputs, dev):
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         fn = lambda: eta.attn_prefill(q, k, v, causal=True, out=o, lse=lse)  # noqa: E731
+    elif name == "single_head_f32":
+        q, k, v = inputs.workload_inputs(name, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        fn = lambda: eta.attn_prefill(q, k, v, causal=False, out=o, lse=lse)  # noqa: E731
     elif name == "backward_4k":
         q, k, v, do = inputs.workload_inputs("causal_gqa_backward_4k", dev)
         o, lse = eta.attn_prefill(q, k, v, causal=True)

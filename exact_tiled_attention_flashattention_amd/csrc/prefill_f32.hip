@@ -3,21 +3,25 @@
 // optimisation", sections "tiling trick" and "Build it, step 2").
 //
 // The fp32 path exists for exactness checks at fp32 tolerance and for small
-// single-head problems; it is latency-bound, not a throughput path. A
-// workgroup of 256 threads owns 64 query rows of one head; 4 lanes share a
-// row, each holding a quarter of q and of the output (interleaved 16-byte
-// chunks so the 4 lanes read adjacent LDS words). K/V tiles of 32 keys are
-// staged in LDS and broadcast to all rows. A row's dot product is finished
-// with two lane exchanges; the running max/sum update is the same as in the
-// bf16 kernel.
+// single-head problems, where the time is latency: a launch, one round of
+// loads and a chain of dependent arithmetic per row. So the work is spread
+// thin. A workgroup owns 16 query rows of one head (4 lanes per row, each
+// holding a quarter of q and of the output in interleaved 16-byte chunks)
+// and its 4 waves take every fourth tile of keys each, so a row's chain of
+// keys is split four ways. Each wave streams its own tiles through a private
+// double buffer in LDS with direct global->LDS loads (no workgroup barrier
+// inside the loop), runs the running (max, sum) update over them, and at the
+// end the four partial results of each row are merged through LDS with the
+// same log-sum-exp weights as the split-KV decode.
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-constexpr int kRows = 64;
-constexpr int kKeys = 32;
+constexpr int kRows = 16;    // query rows per workgroup
+constexpr int kWaves = 4;    // key-parallel waves per workgroup
+constexpr int kBufferFlags = 0x00020000;
 
 struct F32Params {
   const float* q;
@@ -33,13 +37,20 @@ struct F32Params {
 
 template <int D>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Params p) {
-  constexpr int NE = D / 16;  // float4 chunks per lane
-  __shared__ __attribute__((aligned(16))) float kt[kKeys * D];
-  __shared__ __attribute__((aligned(16))) float vt[kKeys * D];
+  constexpr int NE = D / 16;       // float4 chunks per lane
+  constexpr int TK = 2048 / D;     // keys per staged tile (8 KiB of K, 8 KiB of V)
+  constexpr int TILEF = TK * D;    // floats per K (or V) tile
+  constexpr int NL = TILEF / 256;  // 16-byte direct loads per lane per tile and tensor
+  // per wave: [buffer 0: K, V][buffer 1: K, V]; reused for the final merge
+  __shared__ __attribute__((aligned(16))) float lds[kWaves * 4 * TILEF];
+  __shared__ float mrow[kWaves][kRows];
+  __shared__ float lrow[kWaves][kRows];
 
   const int tid = threadIdx.x;
-  const int part = tid & 3;
-  const int row = tid >> 2;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int part = lane & 3;
+  const int row = lane >> 2;
   const int qblk = blockIdx.x % p.n_qblk;
   const int bh = blockIdx.x / p.n_qblk;
   const int hq = bh % p.Hq;
@@ -62,31 +73,55 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Params p) {
     const long long lim = (long long)last + p.q_offset + 1;
     if (lim < kend) kend = (int)(lim < 0 ? 0 : lim);
   }
+  const int ntiles = (kend + TK - 1) / TK;
   const long long lim_row = (long long)my_q + p.q_offset;
   const float* kg = p.k + ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
   const float* vg = p.v + ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
+  float* wl = lds + wave * 4 * TILEF;
 
-  float m_run = neg_inf();
-  float l_run = 0.f;
-  for (int k0 = 0; k0 < kend; k0 += kKeys) {
-    __syncthreads();
-    for (int c = tid; c < kKeys * D / 4; c += 256) {
-      const int r = c / (D / 4);
-      const int col = (c % (D / 4)) * 4;
-      f32x4_t kk = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-      if (k0 + r < p.Nk) {
-        kk = *reinterpret_cast<const f32x4_t*>(kg + (long long)(k0 + r) * D + col);
-        vv = *reinterpret_cast<const f32x4_t*>(vg + (long long)(k0 + r) * D + col);
-      }
-      *reinterpret_cast<f32x4_t*>(kt + r * D + col) = kk;
-      *reinterpret_cast<f32x4_t*>(vt + r * D + col) = vv;
+  // tile t of this head into buffer `buf` of this wave: lane l moves bytes
+  // [16 l + 1024 i, +16) of the tile; keys past Nk read as zeros (the
+  // resource ends at the head's last key)
+  auto stage = [&](int t, int buf) __attribute__((always_inline)) {
+    const long long off = (long long)t * TILEF;
+    const long long left = ((long long)p.Nk * D - off) * 4;
+    const int range = (int)(left < 0 ? 0 : (left > TILEF * 4 ? TILEF * 4 : left));
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kg + off), 0, range, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vg + off), 0, range, kBufferFlags);
+    float* kd = wl + buf * 2 * TILEF;
+    float* vd = kd + TILEF;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (ATTN_LDS void*)(kd + 256 * i), 16,
+                                               16 * lane + 1024 * i, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (ATTN_LDS void*)(vd + 256 * i), 16,
+                                               16 * lane + 1024 * i, 0, 0, 0);
     }
-    __syncthreads();
+  };
 
-    float s[kKeys];
+  float m_run = neg_inf();  // base-2 running max of this row (this wave's keys)
+  float l_run = 0.f;
+  int buf = 0;
+  if (wave < ntiles) stage(wave, 0);
+  for (int t = wave; t < ntiles; t += kWaves) {
+    if (t + kWaves < ntiles) {
+      stage(t + kWaves, buf ^ 1);
+      // vmcnt(2 NL): all but the next tile's loads have landed
+      __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * NL) & 15) | (((2 * NL) >> 4) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    asm volatile("" ::: "memory");  // the tile's LDS reads stay after the wait
+    const float* kt = wl + buf * 2 * TILEF;
+    const float* vt = kt + TILEF;
+    const int k0 = t * TK;
+
+    float s[TK];
     float mx = neg_inf();
 #pragma unroll
-    for (int j = 0; j < kKeys; ++j) {
+    for (int j = 0; j < TK; ++j) {
       float a = 0.f;
 #pragma unroll
       for (int e = 0; e < NE; ++e) {
@@ -111,7 +146,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Params p) {
 #pragma unroll
     for (int e = 0; e < NE; ++e) ov[e] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kKeys; ++j) {
+    for (int j = 0; j < TK; ++j) {
       const float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], p.c, -m_use));
       rs += pj;
 #pragma unroll
@@ -124,17 +159,47 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Params p) {
       }
     }
     l_run = l_run * alpha + rs;
+    buf ^= 1;
   }
 
-  if (my_q < p.Nq) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // ---- merge the four waves' partial results of each row -----------------------
+  // O = Σ_w 2^(m_w − M) O_w / Σ_w 2^(m_w − M) l_w with M = max_w m_w (an
+  // empty partial has m_w = −inf and weight 0)
+  __syncthreads();  // every wave is done with its tiles: the buffers become the merge area
+  float* mo = lds + (wave * kRows + row) * D;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) *reinterpret_cast<f32x4_t*>(mo + 4 * (part + 4 * e)) = ov[e];
+  if (part == 0) {
+    mrow[wave][row] = m_run;
+    lrow[wave][row] = l_run;
+  }
+  __syncthreads();
+  if (wave == 0 && my_q < p.Nq) {
+    float M = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mrow[w][row]);
+    const float M_use = (M == neg_inf()) ? 0.f : M;
+    float L = 0.f;
+    f32x4_t acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(mrow[w][row] - M_use);  // 0 for an empty partial
+      L += wt * lrow[w][row];
+      const float* src = lds + (w * kRows + row) * D;
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+        acc[e] += wt * *reinterpret_cast<const f32x4_t*>(src + 4 * (part + 4 * e));
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
     float* op = p.o + (((long long)b * p.Hq + hq) * p.Nq + my_q) * D;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
-      *reinterpret_cast<f32x4_t*>(op + 4 * (part + 4 * e)) = ov[e] * inv;
+      *reinterpret_cast<f32x4_t*>(op + 4 * (part + 4 * e)) = acc[e] * inv;
     if (part == 0 && p.lse != nullptr)
       p.lse[((long long)b * p.Hq + hq) * p.Nq + my_q] =
-          l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2 : neg_inf();
+          L > 0.f ? (M + __builtin_amdgcn_logf(L)) * kLn2 : neg_inf();
   }
 }
 

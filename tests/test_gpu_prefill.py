@@ -39,6 +39,9 @@ def test_single_head_f32_workload():
     (1, 4, 2, 150, 150, 128, True, 0),
     (2, 3, 1, 65, 300, 128, True, 235),
     (1, 1, 1, 1, 1, 64, False, 0),
+    (1, 2, 1, 40, 30, 64, True, -10),     # rows 0..9 see no key
+    (1, 1, 1, 300, 1000, 128, False, 0),  # many tiles per wave, ragged tail
+    (2, 4, 4, 17, 33, 64, True, 16),      # fewer tiles than waves
 ])
 def test_f32_shapes(B, Hq, Hkv, Nq, Nk, d, causal, off):
     dev = need_gpu()
