@@ -331,13 +331,13 @@ def main():
         "ms": round(ms4, 5), "GB/s": round(bytes4 / (ms4 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kv_bytes": bytes4,
-        "traffic_partial_kernel": counter_traffic("splitkv_decode_32k", "decode_partial_kernel<128>",
+        "traffic_partial_kernel": counter_traffic("splitkv_decode_32k", "decode_partial_kernel<128,false>",
                                                   ["common.h", "decode.hip"])}
     result_workloads["paged_decode_q4"] = {
         "ms": round(ms5, 5), "GB/s": round(bytes5 / (ms5 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes5 / (ms5 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kv_bytes": bytes5, "kv_append_ms": round(msa, 5),
-        "traffic_partial_kernel": counter_traffic("paged_decode_q4", "decode_partial_kernel<128>",
+        "traffic_partial_kernel": counter_traffic("paged_decode_q4", "decode_partial_kernel<128,false>",
                                                   ["common.h", "decode.hip"])}
 
     # long-context prefill and the fp32 single-head case, in their own loops
@@ -448,7 +448,10 @@ def main():
         "ms": round(ms7, 5), "GB/s": round(bytes7 / (ms7 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes7 / (ms7 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kv_bytes": bytes7, "kv_append_ms": round(t7.mean_ms("a"), 5),
-        "speedup_vs_bf16_cache": round(ms5 / ms7, 3)}
+        "speedup_vs_bf16_cache": round(ms5 / ms7, 3),
+        "traffic_partial_kernel": counter_traffic("paged_decode_q4_fp8",
+                                                  "decode_partial_kernel<128,true>",
+                                                  ["common.h", "decode.hip"])}
     del p7, o7, l7, ws7
     torch.cuda.empty_cache()
     q1, k1, v1 = inputs.workload_inputs("single_head_f32", dev)
