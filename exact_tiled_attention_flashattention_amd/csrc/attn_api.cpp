@@ -187,6 +187,7 @@ int attn_prefill_backward(const void* q, const void* k, const void* v, const voi
   if (workspace == nullptr || misaligned16(workspace) || workspace_bytes_given < pl.bytes)
     return ATTN_EWORKSPACE;
   attn::BackwardArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace),
+                       reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.lrow_offset),
                        B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, q_offset};
   a.nsplit = pl.nsplit;
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_offset);

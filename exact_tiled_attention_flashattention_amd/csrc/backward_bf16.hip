@@ -32,6 +32,8 @@
 // XOR-swizzled LDS layout in which both the row reads (MFMA A operand) and
 // the transposing reads are conflict-free, double-buffered with one barrier
 // per tile.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -53,6 +55,7 @@ struct BwdParams {
   __bf16* dk;
   __bf16* dv;
   float* drow;  // [B, Hq, Nq] workspace: D_i = dO_i · O_i
+  float* lrow;  // [B, Hq, Nq] workspace: the row's base-2 LSE (+inf for a row that saw no key)
   int B, Hq, Hkv, Nq, Nk;
   int G;       // Hq / Hkv
   int hw;      // heads per dQ workgroup (1, 2 or 4)
@@ -203,7 +206,10 @@ void bwd_dq_kernel(BwdParams p) {
   const float drow = sum_across_halves(dsum);
   const long long ridx = ((long long)b * p.Hq + hq) * p.Nq + my_q;
   const float lse2 = row_ok ? lse2_of(p.lse[ridx]) : __builtin_inff();
-  if (row_ok && g == 0) p.drow[ridx] = drow;
+  if (row_ok && g == 0) {
+    p.drow[ridx] = drow;
+    p.lrow[ridx] = lse2;
+  }
 
   const long long kv_base = ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
   const long long kv_bytes = (long long)p.Nk * D * 2;
@@ -391,8 +397,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     const long long left = (long long)p.Nq - r0;  // rows of the head from there on
     load_tile<D>(p.q + (hbase + r0) * D, left * D * 2, qdst, wave, lane);
     load_tile<D>(p.dout + (hbase + r0) * D, left * D * 2, odst, wave, lane);
-    if (wave < 2) {  // wave 0: LSE of the 64 rows, wave 1: D (rows past Nq read 0)
-      const float* srcp = (wave == 0 ? p.lse : p.drow) + hbase + r0;
+    if (wave < 2) {  // wave 0: base-2 LSE of the 64 rows, wave 1: D (rows past Nq read 0)
+      const float* srcp = (wave == 0 ? p.lrow : p.drow) + hbase + r0;
       const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(srcp), 0, (int)(left >= kTile ? kTile * 4 : left * 4), kBufferFlags);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (ATTN_LDS void*)(ldst + wave * kTile), 4,
@@ -400,12 +406,12 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  auto step = [&](int s, const char* ql, const char* ol, const float* ll)
+  // a key of this wave is hidden from tile row `row` iff my_key - q_offset > row
+  // (both sides fit in 32 bits: keys < 2^24 and |q_offset| <= 2^30)
+  const int kq = my_key - p.q_offset;
+  auto step = [&](bool masked, int s, const char* ql, const char* ol, const float* ll)
       __attribute__((always_inline)) {
-    const int qt = qt_lo + s % per_head;
-    const int qrow0 = qt * kTile;
-    // under a causal mask, pairs are hidden only where a row precedes a key
-    const bool masked = CAUSAL && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
+    const int qrow0 = (qt_lo + s % per_head) * kTile;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
@@ -433,11 +439,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * m + r;
           float x = sc[i];
-          if (masked) {
-            const int row = qrow0 + qb * 32 + 8 * m + 4 * g + r;
-            if ((long long)my_key > (long long)row + p.q_offset) x = neg_inf();
-          }
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -lse2_of(l4[r])));
+          if (masked && kq > qrow0 + qb * 32 + 8 * m + 4 * g + r) x = neg_inf();
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -l4[r]));
           pv[r] = pr;
           dv[r] = pr * (dp[i] - d4[r]);
         }
@@ -475,7 +478,10 @@ void bwd_dkdv_kernel(BwdParams p) {
       __syncthreads();                     // ... for every wave; step s-1's buffers are free
       if (s + 1 < nsteps) issue(s + 1, (s & 1) ? qb0 : qb1, (s & 1) ? ob0 : ob1,
                                 (s & 1) ? ld0 : ld1);
-      step(s, qc, oc, lc);
+      // under a causal mask, pairs are hidden only where a row precedes a key
+      const int qrow0 = (qt_lo + s % per_head) * kTile;
+      const bool masked = CAUSAL && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
+      step(masked, s, qc, oc, lc);
     }
   }
 
@@ -587,9 +593,12 @@ BackwardPlan plan_backward(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
       break;
     }
   }
-  const size_t drow = (size_t)B * Hq * Nq * sizeof(float);
-  pl.part_offset = (drow + 255) / 256 * 256;
-  if (pl.part_offset == 0) pl.part_offset = 256;
+  // D at 0, the base-2 LSE at lrow_offset, then the partial sums; each part
+  // 256-byte aligned and at least 256 bytes
+  size_t rows = ((size_t)B * Hq * Nq * sizeof(float) + 255) / 256 * 256;
+  if (rows == 0) rows = 256;
+  pl.lrow_offset = rows;
+  pl.part_offset = 2 * rows;
   const size_t part = pl.nsplit > 1 ? 2ull * pl.nsplit * B * Hkv * (size_t)Nk * d * sizeof(float)
                                     : 0;
   pl.bytes = pl.part_offset + part;
@@ -608,6 +617,7 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t s) {
   bp.dk = static_cast<__bf16*>(a.dk);
   bp.dv = static_cast<__bf16*>(a.dv);
   bp.drow = a.drow;
+  bp.lrow = a.lrow;
   bp.B = a.B;
   bp.Hq = a.Hq;
   bp.Hkv = a.Hkv;

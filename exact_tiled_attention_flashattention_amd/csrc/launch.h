@@ -79,7 +79,8 @@ struct BackwardArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* drow;  // workspace: [B, Hq, Nq] f32
+  float* drow;  // workspace: [B, Hq, Nq] f32, D of every row
+  float* lrow;  // workspace: [B, Hq, Nq] f32, base-2 LSE of every row
   int B, Hq, Hkv, Nq, Nk, d;
   float scale;
   int causal;
@@ -92,8 +93,9 @@ struct BackwardArgs {
 // the partial sums when nsplit > 1).
 struct BackwardPlan {
   int nsplit = 1;
-  size_t part_offset = 256;
-  size_t bytes = 256;
+  size_t lrow_offset = 256;
+  size_t part_offset = 512;
+  size_t bytes = 512;
 };
 BackwardPlan plan_backward(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                            int q_offset, int compute_units);

@@ -282,16 +282,17 @@ def test_backward_rejects_bad_arguments():
 def test_backward_workspace_size():
     lib = eta.library()
     f = lib.attn_prefill_backward_workspace_bytes
-    # D alone when every K/V head's group fits one workgroup (MHA, or enough work)
-    assert f(1, 8, 8, 4096, 4096, 128, 1, 0) == 8 * 4096 * 4
-    assert f(1, 32, 8, 32768, 32768, 128, 1, 0) == 32 * 32768 * 4
+    # D and the base-2 LSE of every row alone when every K/V head's group fits
+    # one workgroup (MHA, or enough work)
+    assert f(1, 8, 8, 4096, 4096, 128, 1, 0) == 2 * 8 * 4096 * 4
+    assert f(1, 32, 8, 32768, 32768, 128, 1, 0) == 2 * 32 * 32768 * 4
     # the 4k causal GQA workload shares each group between workgroups: D plus
     # the fp32 partial sums of dK and dV for every share
     n = f(1, 32, 8, 4096, 4096, 128, 1, 0)
-    extra = n - 32 * 4096 * 4
+    extra = n - 2 * 32 * 4096 * 4
     plane = 8 * 4096 * 128 * 4
     assert extra > 0 and extra % (2 * plane) == 0 and extra // (2 * plane) in (2, 4)
-    assert f(1, 1, 1, 1, 1, 64, 0, 0) == 256
+    assert f(1, 1, 1, 1, 1, 64, 0, 0) == 512
     assert f(-1, 1, 1, 1, 1, 64, 0, 0) == 0
     assert f(1, 4, 3, 1, 1, 64, 0, 0) == 0          # Hq % Hkv != 0
     assert f(1, 4, 2, 1, 1, 96, 0, 0) == 0          # head dim not built
