@@ -225,11 +225,25 @@ def cpu_baseline(q, k, v, min_seconds=10.0, max_heads=128):
         done += 1
     dt = time.perf_counter() - t0
     flops = prefill_flops(1, done, q.shape[2], d)
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} head passes (heads taken in order, cycling over the {Hq}), all "
-                      f"{q.shape[2]} rows each, of the causal GQA 4k prefill (fp64 numpy, "
-                      f"{dt:.1f} s)"}
+    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{done} head passes (heads taken in order, cycling over the {Hq}), all "
+                     f"{q.shape[2]} rows each, of the causal GQA 4k prefill (fp64 numpy, "
+                     f"{dt:.1f} s)"}
+    # the same oracle on one core: one head pass with BLAS limited to one thread
+    try:
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            oracle.attention_rows(qc[0, 0], np.arange(q.shape[2]), kc[0, 0], vc[0, 0],
+                                  1.0 / math.sqrt(d), True)
+            d1 = time.perf_counter() - t1
+        out["single_core_value"] = round(prefill_flops(1, 1, q.shape[2], d) / d1 / 1e12, 6)
+        out["single_core_sample"] = f"1 head pass of the same workload on 1 thread ({d1:.1f} s)"
+    except Exception:  # threadpoolctl missing: no single-core figure
+        pass
+    return out
 
 
 def main():
