@@ -71,6 +71,10 @@ def _run(dev, seed, B, Hq, Hkv, Nq, Nk, d, causal, q_offset, kv_heads=None):
     (2, 2, 2, 33, 257, 128, False, 0),
     (1, 6, 2, 190, 190, 64, True, 0),      # G = 3: two heads per workgroup slot
     (1, 8, 2, 64, 16384, 128, False, 0),   # enough key blocks that each group stays whole
+    (1, 32, 4, 96, 96, 128, True, 0),      # G = 8: the group shared by several workgroups
+    (1, 4, 2, 520, 520, 64, True, 0),      # d = 64 over many key blocks
+    (2, 4, 1, 300, 130, 128, False, 0),    # more query rows than keys
+    (1, 2, 1, 1, 1, 128, True, 0),         # one row, one key
 ])
 def test_backward_matches_oracle(B, Hq, Hkv, Nq, Nk, d, causal, off):
     dev = need_gpu()
