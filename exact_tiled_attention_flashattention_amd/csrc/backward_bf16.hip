@@ -19,21 +19,21 @@
 //     constants, and dQᵀ += Kᵀ·dSᵀ with Kᵀ read through the transposing LDS
 //     read. It also writes D to the workspace.
 //   * bwd_dkdv_kernel: one workgroup per (128-key block, K/V head, share of
-//     the group's query heads). A wave owns 32 keys, holds its K and V rows
-//     in registers and streams the Q / dO tiles of its query heads through
-//     LDS; it computes S = Q·Kᵀ and dP = dO·Vᵀ (one key per lane), then
-//     dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with dOᵀ, Qᵀ read through the transposing
-//     LDS read. The sum over those heads happens in the accumulators. When
-//     the group is shared by several workgroups (so that, under a causal
-//     mask, no workgroup holds far more than its share of the work), each
-//     writes fp32 partial sums and bwd_reduce_kernel adds them in a fixed
-//     order: the result does not depend on timing.
+//     the group's query heads), 8 waves: each 32-key slice has a dV wave and
+//     a dK wave, the dK wave one tile step behind. The dV wave holds the
+//     slice's K rows, computes S = Q·Kᵀ (one key per lane), P, and
+//     dVᵀ += dOᵀ·P, and leaves P in LDS; the dK wave holds the V rows,
+//     computes dP = dO·Vᵀ, dS = P ∘ (dP − D) from that P, and dKᵀ += Qᵀ·dS.
+//     dOᵀ and Qᵀ come from the transposing LDS read. The sum over the query
+//     heads happens in the accumulators. When the group is shared by several
+//     workgroups (so that, under a causal mask, no workgroup holds far more
+//     than its share of the work), each writes fp32 partial sums and
+//     bwd_reduce_kernel adds them in a fixed order: the result does not
+//     depend on timing.
 // Tiles are 64 rows of D bf16, loaded straight from global memory into an
 // XOR-swizzled LDS layout in which both the row reads (MFMA A operand) and
-// the transposing reads are conflict-free, double-buffered with one barrier
-// per tile.
-#include <type_traits>
-
+// the transposing reads are conflict-free, double-buffered (triple-buffered
+// in the dK/dV kernel) with one barrier per tile.
 #include "common.h"
 #include "launch.h"
 
@@ -68,6 +68,7 @@ struct BwdParams {
   float c;     // scale * log2(e)
   float scale;
   int q_offset;
+  int causal;
 };
 
 // Tile rows live in LDS unpadded (D*2 bytes per row) with the 16-byte chunks
@@ -314,29 +315,35 @@ void bwd_dq_kernel(BwdParams p) {
 }
 
 // ============================================================================
-// dK, dV
+// dK, dV with each 32-key slice shared by two waves and the two halves of
+// the work one tile step apart. The dV wave computes S = Q·Kᵀ, P (masked,
+// packed to bf16) and dVᵀ += dOᵀ·P, and leaves P in LDS; one step later the
+// dK wave computes dP = dO·Vᵀ, dS = P ∘ (dP − D) from that P, and
+// dKᵀ += Qᵀ·dS. Each wave holds one accumulator set and one of K, V, so two
+// waves fit a SIMD; no product is computed twice. Tiles are triple-buffered
+// (the dK wave reads step s−1 while the dV wave reads step s and step s+1 is
+// loading); the one barrier per step orders every hand-over.
 // ============================================================================
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NDC = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TILE = kTile * D * 2;
-  __shared__ __attribute__((aligned(1024))) char qb0[TILE];
-  __shared__ __attribute__((aligned(1024))) char qb1[TILE];
-  __shared__ __attribute__((aligned(1024))) char ob0[TILE];  // dO tiles
-  __shared__ __attribute__((aligned(1024))) char ob1[TILE];
-  __shared__ __attribute__((aligned(16))) float ld0[2 * kTile];  // LSE then D of the tile rows
-  __shared__ __attribute__((aligned(16))) float ld1[2 * kTile];
+  __shared__ __attribute__((aligned(1024))) char qbuf[3][TILE];
+  __shared__ __attribute__((aligned(1024))) char obuf[3][TILE];  // dO tiles
+  __shared__ __attribute__((aligned(16))) float lbuf[3][2 * kTile];  // base-2 LSE, then D
+  // P of a step, bf16 pairs in S register order: [buffer][slice][half][lane][8]
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf[2][kWaves][2][64][8];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave8 >> 2;  // 0: dV (and P), 1: dK
+  const int wave = wave8 & 3;   // key slice
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // key blocks in increasing order: under a causal mask the first blocks
-  // see the most query rows, so the longest workgroups start first
   const int per_k = p.B * p.Hkv * p.nsplit;
   const int kblk = blockIdx.x / per_k;
   int rest = blockIdx.x - kblk * per_k;
@@ -344,29 +351,21 @@ void bwd_dkdv_kernel(BwdParams p) {
   rest /= p.nsplit;
   const int kvh = rest % p.Hkv;
   const int b = rest / p.Hkv;
-  const int gs = p.G / p.nsplit;  // query heads of this workgroup
-  const int k0 = kblk * (kWaves * 32);        // first key of the workgroup
-  const int kw0 = k0 + wave * 32;              // first key of the wave
+  const int gs = p.G / p.nsplit;
+  const int k0 = kblk * (kWaves * 32);
+  const int kw0 = k0 + wave * 32;
   const int my_key = kw0 + l32;
 
-  // K and V rows of the wave's keys as B operands: lane holds key my_key,
-  // d = 16*dc + 8*g + j
+  // K rows (dV role) or V rows (dK role) of the slice as B operands
   const long long kv_base = ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
-  bf16x8_t kf[NDC], vf[NDC];
+  const __bf16* kvsrc = role == 0 ? p.k : p.v;
+  bf16x8_t kv[NDC];
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) {
-    if (my_key < p.Nk) {
-      kf[dc] = *reinterpret_cast<const bf16x8_t*>(p.k + kv_base + (long long)my_key * D + 16 * dc +
-                                                   8 * g);
-      vf[dc] = *reinterpret_cast<const bf16x8_t*>(p.v + kv_base + (long long)my_key * D + 16 * dc +
-                                                   8 * g);
-    } else {
-      kf[dc] = bf16x8_t{};
-      vf[dc] = bf16x8_t{};
-    }
-  }
+  for (int dc = 0; dc < NDC; ++dc)
+    kv[dc] = my_key < p.Nk ? *reinterpret_cast<const bf16x8_t*>(
+                                 kvsrc + kv_base + (long long)my_key * D + 16 * dc + 8 * g)
+                           : bf16x8_t{};
 
-  // query tiles that can see any key of the block: rows i >= k0 - q_offset
   int qt_lo = 0;
   if (CAUSAL) {
     const long long first_row = (long long)k0 - p.q_offset;
@@ -376,137 +375,157 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int per_head = n_qt > qt_lo ? n_qt - qt_lo : 0;
   const int nsteps = per_head * gs;
 
-  f32x16_t acck[NDB], accv[NDB];
+  f32x16_t acc[NDB];  // dVᵀ (role 0) or dKᵀ (role 1)
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    acck[db] = f32x16_t{};
-    accv[db] = f32x16_t{};
-  }
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
   const int grp = lane >> 4;
   const int src = lane & 15;
   const int tr_row = src >> 2;
   const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
+  const int kq = my_key - p.q_offset;
 
-  // step s: query head kvh*G + split*gs + s / per_head, tile qt_lo + s % per_head
-  auto issue = [&](int s, char* qdst, char* odst, float* ldst) __attribute__((always_inline)) {
+  // step s's tiles into buffer s % 3, issued by the dV waves
+  auto issue = [&](int s) __attribute__((always_inline)) {
     const int hq = kvh * p.G + split * gs + s / per_head;
     const int qt = qt_lo + s % per_head;
     const long long hbase = ((long long)b * p.Hq + hq) * (long long)p.Nq;
-    const long long r0 = (long long)qt * kTile;   // first row of the tile
-    const long long left = (long long)p.Nq - r0;  // rows of the head from there on
-    load_tile<D>(p.q + (hbase + r0) * D, left * D * 2, qdst, wave, lane);
-    load_tile<D>(p.dout + (hbase + r0) * D, left * D * 2, odst, wave, lane);
-    if (wave < 2) {  // wave 0: base-2 LSE of the 64 rows, wave 1: D (rows past Nq read 0)
+    const long long r0 = (long long)qt * kTile;
+    const long long left = (long long)p.Nq - r0;
+    const int bi = s % 3;
+    load_tile<D>(p.q + (hbase + r0) * D, left * D * 2, qbuf[bi], wave, lane);
+    load_tile<D>(p.dout + (hbase + r0) * D, left * D * 2, obuf[bi], wave, lane);
+    if (wave < 2) {
       const float* srcp = (wave == 0 ? p.lrow : p.drow) + hbase + r0;
       const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(srcp), 0, (int)(left >= kTile ? kTile * 4 : left * 4), kBufferFlags);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (ATTN_LDS void*)(ldst + wave * kTile), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (ATTN_LDS void*)(lbuf[bi] + wave * kTile), 4,
                                                4 * lane, 0, 0, 0);
     }
   };
 
-  // a key of this wave is hidden from tile row `row` iff my_key - q_offset > row
-  // (both sides fit in 32 bits: keys < 2^24 and |q_offset| <= 2^30)
-  const int kq = my_key - p.q_offset;
-  auto step = [&](bool masked, int s, const char* ql, const char* ol, const float* ll)
-      __attribute__((always_inline)) {
+  // dV role, step s: S, P (left in LDS for the dK wave), dVᵀ += dOᵀ P
+  auto step_v = [&](int s) __attribute__((always_inline)) {
+    const char* ql = qbuf[s % 3];
+    const char* ol = obuf[s % 3];
+    const float* ll = lbuf[s % 3];
     const int qrow0 = (qt_lo + s % per_head) * kTile;
+    // (decided at run time in both instantiations: with a compile-time false
+    // the non-causal schedule keeps more loads in flight and spills)
+    const bool masked = p.causal != 0 && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16_t sc = f32x16_t{}, dp = f32x16_t{};
+      f32x16_t sc = f32x16_t{};
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
         const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(
             ql + lds_off<D>(qb * 32 + l32, 16 * dc + 8 * g));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[dc], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kv[dc], sc, 0, 0, 0);
       }
+      uint32_t pk[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(ll + qb * 32 + 8 * m + 4 * g);
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = sc[4 * m + r];
+          if (masked && kq > qrow0 + qb * 32 + 8 * m + 4 * g + r) x = neg_inf();
+          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -l4[r]));
+        }
+        pk[2 * m] = pack_bf16x2(pv[0], pv[1]);
+        pk[2 * m + 1] = pack_bf16x2(pv[2], pv[3]);
+      }
+      uint32_t* pdst = pbuf[s & 1][wave][qb][lane];
+      *reinterpret_cast<u32x4_t*>(pdst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+      *reinterpret_cast<u32x4_t*>(pdst + 4) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4_t w4 = {pk[4 * hf], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
+        const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, w4);
+        const int r0 = qb * 32 + 16 * hf + 4 * g + tr_row;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ol, r0, 32 * db + tr_col),
+                                                            bo, acc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // dK role, step s (one step behind): dP, dS = P ∘ (dP − D), dKᵀ += Qᵀ dS
+  auto step_k = [&](int s) __attribute__((always_inline)) {
+    const char* ql = qbuf[s % 3];
+    const char* ol = obuf[s % 3];
+    const float* ll = lbuf[s % 3];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16_t dp = f32x16_t{};
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
         const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(
             ol + lds_off<D>(qb * 32 + l32, 16 * dc + 8 * g));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[dc], dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, kv[dc], dp, 0, 0, 0);
       }
-      // accumulator i holds row qb*32 + 8*(i/4) + 4*g + i%4 of the tile
-      uint32_t pp[8], pd[8];
+      const uint32_t* psrc = pbuf[s & 1][wave][qb][lane];
+      const u32x4_t p0 = *reinterpret_cast<const u32x4_t*>(psrc);
+      const u32x4_t p1 = *reinterpret_cast<const u32x4_t*>(psrc + 4);
+      const uint32_t pp[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      uint32_t pd[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(ll + qb * 32 + 8 * m + 4 * g);
         const f32x4_t d4 =
             *reinterpret_cast<const f32x4_t*>(ll + kTile + qb * 32 + 8 * m + 4 * g);
-        float pv[4], dv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * m + r;
-          float x = sc[i];
-          if (masked && kq > qrow0 + qb * 32 + 8 * m + 4 * g + r) x = neg_inf();
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -l4[r]));
-          pv[r] = pr;
-          dv[r] = pr * (dp[i] - d4[r]);
-        }
-        pp[2 * m] = pack_bf16x2(pv[0], pv[1]);
-        pp[2 * m + 1] = pack_bf16x2(pv[2], pv[3]);
-        pd[2 * m] = pack_bf16x2(dv[0], dv[1]);
-        pd[2 * m + 1] = pack_bf16x2(dv[2], dv[3]);
+        const float e0 = bf16_lo(pp[2 * m]) * (dp[4 * m] - d4[0]);
+        const float e1 = bf16_hi(pp[2 * m]) * (dp[4 * m + 1] - d4[1]);
+        const float e2 = bf16_lo(pp[2 * m + 1]) * (dp[4 * m + 2] - d4[2]);
+        const float e3 = bf16_hi(pp[2 * m + 1]) * (dp[4 * m + 3] - d4[3]);
+        pd[2 * m] = pack_bf16x2(e0, e1);
+        pd[2 * m + 1] = pack_bf16x2(e2, e3);
       }
-      // dVᵀ += dOᵀ P and dKᵀ += Qᵀ dS, 16 rows per MFMA
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const u32x4_t wp = {pp[4 * hf], pp[4 * hf + 1], pp[4 * hf + 2], pp[4 * hf + 3]};
-        const u32x4_t wd = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
-        const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, wp);
-        const bf16x8_t bd = __builtin_bit_cast(bf16x8_t, wd);
+        const u32x4_t w4 = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
+        const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, w4);
         const int r0 = qb * 32 + 16 * hf + 4 * g + tr_row;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ol, r0, 32 * db + tr_col),
-                                                             bp, accv[db], 0, 0, 0);
-          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ql, r0, 32 * db + tr_col),
-                                                             bd, acck[db], 0, 0, 0);
-        }
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ql, r0, 32 * db + tr_col),
+                                                            bo, acc[db], 0, 0, 0);
       }
     }
   };
 
   if (nsteps > 0) {
-    issue(0, qb0, ob0, ld0);
-    for (int s = 0; s < nsteps; ++s) {
-      char* qc = (s & 1) ? qb1 : qb0;
-      char* oc = (s & 1) ? ob1 : ob0;
-      float* lc = (s & 1) ? ld1 : ld0;
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step s's tiles have landed
-      __syncthreads();                     // ... for every wave; step s-1's buffers are free
-      if (s + 1 < nsteps) issue(s + 1, (s & 1) ? qb0 : qb1, (s & 1) ? ob0 : ob1,
-                                (s & 1) ? ld0 : ld1);
-      // under a causal mask, pairs are hidden only where a row precedes a key
-      const int qrow0 = (qt_lo + s % per_head) * kTile;
-      const bool masked = CAUSAL && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
-      step(masked, s, qc, oc, lc);
+    if (role == 0) issue(0);
+    for (int it = 0; it <= nsteps; ++it) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step it's tiles have landed
+      __syncthreads();  // ... for every wave; step it-2's buffers and it-1's P are handed over
+      if (role == 0) {
+        if (it + 1 < nsteps) issue(it + 1);
+        if (it < nsteps) step_v(it);
+      } else if (it >= 1) {
+        step_k(it - 1);
+      }
     }
   }
 
   if (my_key < p.Nk) {
     const long long off = kv_base + (long long)my_key * D;
-    // nsplit > 1: this workgroup's share, fp32, at [split][b][kvh][key][d]
     const long long plane = (long long)p.B * p.Hkv * p.Nk * D;
-    float* pk = p.part + split * plane + off;
-    float* pv = p.part + (p.nsplit + split) * plane + off;
+    const float f = role == 0 ? 1.f : p.scale;
+    __bf16* out = role == 0 ? p.dv : p.dk;
+    float* part = p.part + ((role == 0 ? p.nsplit : 0) + split) * plane + off;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        f32x4_t k4 = {acck[db][4 * ii] * p.scale, acck[db][4 * ii + 1] * p.scale,
-                      acck[db][4 * ii + 2] * p.scale, acck[db][4 * ii + 3] * p.scale};
-        f32x4_t v4 = {accv[db][4 * ii], accv[db][4 * ii + 1], accv[db][4 * ii + 2],
-                      accv[db][4 * ii + 3]};
+        f32x4_t v4 = {acc[db][4 * ii] * f, acc[db][4 * ii + 1] * f, acc[db][4 * ii + 2] * f,
+                      acc[db][4 * ii + 3] * f};
         const int e = 32 * db + 8 * ii + 4 * g;
-        if (p.nsplit == 1) {
-          *reinterpret_cast<bf16x4_t*>(p.dk + off + e) = __builtin_convertvector(k4, bf16x4_t);
-          *reinterpret_cast<bf16x4_t*>(p.dv + off + e) = __builtin_convertvector(v4, bf16x4_t);
-        } else {
-          *reinterpret_cast<f32x4_t*>(pk + e) = k4;
-          *reinterpret_cast<f32x4_t*>(pv + e) = v4;
-        }
+        if (p.nsplit == 1)
+          *reinterpret_cast<bf16x4_t*>(out + off + e) = __builtin_convertvector(v4, bf16x4_t);
+        else
+          *reinterpret_cast<f32x4_t*>(part + e) = v4;
       }
   }
 }
@@ -547,9 +566,10 @@ hipError_t launch_d(const BwdParams& bp, bool causal, int nq_blocks, int nk_bloc
   }
   if (nk_blocks > 0) {
     if (causal)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(nk_blocks), dim3(kWaves * 64), 0, s, bp);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(nk_blocks), dim3(2 * kWaves * 64), 0, s,
+                         bp);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(nk_blocks), dim3(kWaves * 64), 0, s,
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(nk_blocks), dim3(2 * kWaves * 64), 0, s,
                          bp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || bp.nsplit == 1) return e;
@@ -634,6 +654,7 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t s) {
   bp.c = a.scale * kLog2e;
   bp.scale = a.scale;
   bp.q_offset = a.q_offset;
+  bp.causal = a.causal != 0;
   const long long nq = (long long)bp.n_qblk * a.B * a.Hkv * bp.n_hgrp;
   const long long nk = (long long)bp.n_kblk * a.B * a.Hkv * bp.nsplit;
   if (nq > 0x7fffffffLL || nk > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -5,8 +5,8 @@ The forward kernel's own o and lse feed the backward, as in training. The
 tolerance is derived from where the kernels round: P and dS are rounded to
 bf16 (relative error at most u = 2^-8) before their matrix products, D is
 formed from the bf16-stored O (error at most u times the size of its terms),
-the forward's LSE carries an error well below u, and each gradient is rounded
-once to bf16. Every one of those errors is at most u times a term of the
+the forward's LSE carries an error well below u, the dK/dV kernel forms dS from
+the rounded P, and each gradient is rounded once to bf16. Every one of those errors is at most u times a term of the
 gradient's sum, so element by element
     |gpu - oracle| <= 4u (M + |oracle|) + 1e-6,
 with M the oracle's sum of the absolute values of the terms (its
