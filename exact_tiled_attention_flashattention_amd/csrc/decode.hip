@@ -141,23 +141,15 @@ struct Span {
   bool ok;  // the stretch has storage (its keys may be visible)
 };
 
-#ifndef ATTN_FP8_DEPTH
-#define ATTN_FP8_DEPTH 3
-#endif
-#ifndef ATTN_BF16_DEPTH
-#define ATTN_BF16_DEPTH 2
-#endif
-
-#ifndef ATTN_DECODE_WPE
-#define ATTN_DECODE_WPE 2
-#endif
+// 32-key steps per pipeline: the loads of DEPTH - 1 steps are in flight while
+// one is computed (an E4M3 step is half the bytes, so it keeps more in flight)
+constexpr int kDepthBf16 = 2;
+constexpr int kDepthFp8 = 3;
 
 template <int D, bool KV8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATTN_DECODE_WPE, ATTN_DECODE_WPE))) void decode_partial_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_partial_kernel(DecodeParams p) {
   constexpr int EB = KV8 ? 1 : 2;  // bytes per cached element
-  // steps in the pipeline: an E4M3 step is half the bytes, so it keeps more
-  // of them in flight
-  constexpr int DEPTH = KV8 ? ATTN_FP8_DEPTH : ATTN_BF16_DEPTH;
+  constexpr int DEPTH = KV8 ? kDepthFp8 : kDepthBf16;
   constexpr int NC = D / 32;  // MFMAs per 16 keys for Sᵀ (32 d each)
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;  // query row (Sᵀ/Oᵀ column) of this lane
