@@ -8,11 +8,14 @@
 // the output once. Scores and probabilities live only in registers.
 //
 // Mapping onto CDNA4:
-//   * A workgroup is 4 waves. The waves share one K/V head: with a group of
-//     G = Hq/Hkv query heads ("Effizienz", "GQA im leicht lesbaren Code")
-//     the 4 waves take 4 heads of the group at the same 32 positions (G % 4
-//     == 0), else fewer heads at more positions. Every K/V tile is read from
-//     HBM/L2 once per workgroup and used by all 4 waves.
+//   * A workgroup is 8 waves (4 over a paged cache). The waves share one K/V
+//     head: with a group of G = Hq/Hkv query heads ("Effizienz", "GQA im
+//     leicht lesbaren Code") they take 4 heads of the group at 64 positions
+//     (G % 4 == 0), else fewer heads at more positions. Every K/V tile is
+//     read from HBM/L2 once per workgroup and used by all its waves. One
+//     8-wave workgroup fills a CU (two waves per SIMD), and the two waves
+//     sharing a SIMD step through the same tiles between the same barriers,
+//     so they progress at the same rate.
 //   * Each wave owns 32 query rows. Scores are computed transposed,
 //     Sᵀ = K·Qᵀ, with v_mfma_f32_32x32x16_bf16 (K from LDS as the A
 //     operand, Qᵀ held in registers as the B operand), so each lane holds
@@ -37,7 +40,9 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;
+// waves per workgroup: 8 over [B, H, N, d] slabs, 4 over a token-major cache
+// (one wave per 16-token block of a 64-key tile)
+constexpr int waves_for(bool cache) { return cache ? 4 : 8; }
 constexpr int kBN = 64;         // keys per tile
 constexpr float kTau = 8.0f;    // rescale only when a row max grows by more than 2^8
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, 32-bit dword data
@@ -84,8 +89,10 @@ __device__ __forceinline__ int lds_off(int row, int elem) {  // byte offset of e
 }
 
 template <int D, bool CAUSAL, bool CACHE>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * waves_for(CACHE), 64 * waves_for(CACHE)),
+                          amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillParams p) {
+  constexpr int kWaves = waves_for(CACHE);
   constexpr int NDC = D / 16;              // k-steps of the Q·Kᵀ contraction
   constexpr int NDB = D / 32;              // 32-row blocks of Oᵀ
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
@@ -198,10 +205,10 @@ void prefill_bf16_kernel(PrefillParams p) {
   // wave fills LDS bytes [(wave*NI + i)*1024, +1024), lane l its 16 bytes at
   // +16*l, i.e. physical chunk (lin % CPR) of tile row (lin / CPR); the lane
   // fetches the logical chunk that the swizzle stores there. Rows outside a
-  // resource's range arrive as zeros (those keys are masked). For d = 128 a
-  // 1 KiB instruction covers rows 4*(wave*NI+i) + lane/16, swz = 4*(lane/16) + i;
-  // for d = 64 rows 8*(wave*NI+i) + lane/8, swz = 4*i + lane/16: the
-  // instruction index only flips chunk bits (one XOR).
+  // resource's range arrive as zeros (those keys are masked). With j =
+  // wave*NI + i, a 1 KiB instruction covers rows 4j + lane/16 for d = 128
+  // (swz = 4*(lane/16) + j%4) and rows 8j + lane/8 for d = 64 (swz = 4*(j%2)
+  // + lane/16): the instruction index only flips chunk bits (one XOR).
   constexpr int kXorStep = (D == 128) ? 16 : 64;
   constexpr int RPI = 1024 / (D * 2);  // tile rows per load instruction
   auto lane_offset = [&](int row_bytes) {
@@ -215,12 +222,12 @@ void prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(dst + (wave * NI + i) * 1024),
-                                               16, lb ^ (kXorStep * i),
+                                               16, lb ^ (kXorStep * ((wave * NI + i) & (D == 128 ? 3 : 1))),
                                                soff + i * RPI * row_bytes, 0, 0);
   };
 
   // [B, Hkv, Nk, D] slabs: one resource per K/V head (range Nk rows); the
-  // tile's rows are contiguous, wave w's share starts at row 16w.
+  // tile's rows are contiguous, wave w's share starts at row (64/kWaves)*w.
   const long long kv_base = CACHE ? 0 : ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + kv_base), 0, CACHE ? 0 : p.Nk * D * 2,
@@ -488,7 +495,8 @@ void prefill_bf16_kernel(PrefillParams p) {
 
 template <int D, bool CAUSAL, bool CACHE>
 hipError_t launch_typed(const PrefillParams& pp, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, CACHE>), dim3(nblocks), dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, CACHE>), dim3(nblocks),
+                     dim3(waves_for(CACHE) * 64), 0,
                      s, pp);
   return hipGetLastError();
 }
@@ -518,7 +526,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   pp.Nk = a.Nk;
   pp.G = a.Hq / a.Hkv;
   pp.hw = (pp.G % 4 == 0) ? 4 : ((pp.G % 2 == 0) ? 2 : 1);
-  pp.pw = kWaves / pp.hw;
+  pp.pw = waves_for(a.cache != 0) / pp.hw;
   pp.n_qblk = (a.Nq + 32 * pp.pw - 1) / (32 * pp.pw);
   pp.n_hgrp = pp.G / pp.hw;
   pp.c = a.scale * kLog2e;
