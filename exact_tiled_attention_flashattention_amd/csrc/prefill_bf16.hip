@@ -8,14 +8,13 @@
 // the output once. Scores and probabilities live only in registers.
 //
 // Mapping onto CDNA4:
-//   * A workgroup is 8 waves (4 over a paged cache). The waves share one K/V
-//     head: with a group of G = Hq/Hkv query heads ("Effizienz", "GQA im
-//     leicht lesbaren Code") they take 4 heads of the group at 64 positions
-//     (G % 4 == 0), else fewer heads at more positions. Every K/V tile is
-//     read from HBM/L2 once per workgroup and used by all its waves. One
-//     8-wave workgroup fills a CU (two waves per SIMD), and the two waves
-//     sharing a SIMD step through the same tiles between the same barriers,
-//     so they progress at the same rate.
+//   * A workgroup is 8 waves. The waves share one K/V head: with a group of
+//     G = Hq/Hkv query heads ("Effizienz", "GQA im leicht lesbaren Code")
+//     they take 4 heads of the group at 64 positions (G % 4 == 0), else
+//     fewer heads at more positions. Every K/V tile is read from HBM/L2 once
+//     per workgroup and used by all its waves. One workgroup fills a CU (two
+//     waves per SIMD), and the two waves sharing a SIMD step through the same
+//     tiles between the same barriers, so they progress at the same rate.
 //   * Each wave owns 32 query rows. Scores are computed transposed,
 //     Sᵀ = K·Qᵀ, with v_mfma_f32_32x32x16_bf16 (K from LDS as the A
 //     operand, Qᵀ held in registers as the B operand), so each lane holds
@@ -40,9 +39,7 @@
 namespace attn {
 namespace {
 
-// waves per workgroup: 8 over [B, H, N, d] slabs, 4 over a token-major cache
-// (one wave per 16-token block of a 64-key tile)
-constexpr int waves_for(bool cache) { return cache ? 4 : 8; }
+constexpr int kWaves = 8;  // waves per workgroup: one workgroup fills a CU
 constexpr int kBN = 64;         // keys per tile
 constexpr float kTau = 8.0f;    // rescale only when a row max grows by more than 2^8
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, 32-bit dword data
@@ -89,10 +86,9 @@ __device__ __forceinline__ int lds_off(int row, int elem) {  // byte offset of e
 }
 
 template <int D, bool CAUSAL, bool CACHE>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * waves_for(CACHE), 64 * waves_for(CACHE)),
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves),
                           amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillParams p) {
-  constexpr int kWaves = waves_for(CACHE);
   constexpr int NDC = D / 16;              // k-steps of the Q·Kᵀ contraction
   constexpr int NDB = D / 32;              // 32-row blocks of Oᵀ
   constexpr int CPR = D / 8;               // 16-byte chunks per key row
@@ -236,9 +232,9 @@ void prefill_bf16_kernel(PrefillParams p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + kv_base), 0, CACHE ? 0 : p.Nk * D * 2,
                                         kBufferFlags);
 
-  // Token-major cache: a 64-key tile is four 16-token blocks and wave w loads
-  // block 4t + w of tile t (tile rows 16w..16w+15) through a resource that
-  // ends after the block's last valid row. The block table's entries for 64
+  // Token-major cache: a 64-key tile is four 16-token blocks; each block is
+  // loaded by two waves (8 rows each) through a resource that ends after the
+  // block's last valid row. The block table's entries for 64
   // consecutive blocks sit one per lane in `tab` and are picked with readlane.
   const int rowb = p.Hkv * D * 2;  // bytes between consecutive tokens of one head
   int tab = -1;
@@ -257,7 +253,10 @@ void prefill_bf16_kernel(PrefillParams p) {
     return (e >= 0 && e < p.num_blocks) ? e : -1;
   };
   auto load_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
-    const int jb = 4 * t + wave;
+    // the waves split the tile's four 16-token blocks evenly: wave w loads
+    // rows [16/WB*(w%WB), +16/WB) of block 4t + w/WB, WB = waves per block
+    constexpr int WB = kWaves / 4;
+    const int jb = 4 * t + wave / WB;
     const int e = block_of(jb);
     const int valid = min(kBlockTokens, nk - kBlockTokens * jb);
     const bool ok = e >= 0 && valid > 0;
@@ -268,7 +267,7 @@ void prefill_bf16_kernel(PrefillParams p) {
                  : ((long long)e * kBlockTokens * p.Hkv + kvh) * D;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(pool + row0), 0, ok ? (valid - 1) * rowb + D * 2 : 0, kBufferFlags);
-    load_rows(rs, 0, rowb, dst);
+    load_rows(rs, (wave % WB) * (kBlockTokens / WB) * rowb, rowb, dst);
   };
   // bit q: block 4t + q of tile t has storage (blocks past the sequence count
   // as present; their keys are masked by position)
@@ -496,7 +495,7 @@ void prefill_bf16_kernel(PrefillParams p) {
 template <int D, bool CAUSAL, bool CACHE>
 hipError_t launch_typed(const PrefillParams& pp, int nblocks, hipStream_t s) {
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, CACHE>), dim3(nblocks),
-                     dim3(waves_for(CACHE) * 64), 0,
+                     dim3(kWaves * 64), 0,
                      s, pp);
   return hipGetLastError();
 }
@@ -526,7 +525,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   pp.Nk = a.Nk;
   pp.G = a.Hq / a.Hkv;
   pp.hw = (pp.G % 4 == 0) ? 4 : ((pp.G % 2 == 0) ? 2 : 1);
-  pp.pw = waves_for(a.cache != 0) / pp.hw;
+  pp.pw = kWaves / pp.hw;
   pp.n_qblk = (a.Nq + 32 * pp.pw - 1) / (32 * pp.pw);
   pp.n_hgrp = pp.G / pp.hw;
   pp.c = a.scale * kLog2e;
