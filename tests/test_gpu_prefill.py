@@ -62,6 +62,11 @@ BF16_CASES = [
     (1, 4, 1, 200, 1, 64, False, 0),
     (1, 4, 2, 128, 128, 128, True, -40),   # first 40 rows see no key
     (1, 4, 2, 70, 0, 128, False, 0),       # no keys at all
+    # several causal query blocks per head
+    (1, 8, 2, 300, 300, 64, True, 0),      # odd number of blocks
+    (2, 8, 2, 512, 600, 128, True, 88),    # even number of blocks
+    (1, 4, 1, 300, 300, 128, True, -200),  # the earliest block sees no key
+    (1, 4, 1, 200, 100, 128, True, -400),  # no row sees a key
 ]
 
 
