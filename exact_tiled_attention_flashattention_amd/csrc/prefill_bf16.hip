@@ -234,57 +234,73 @@ void prefill_bf16_kernel(PrefillParams p) {
 
   // Token-major cache: a 64-key tile is four 16-token blocks; each block is
   // loaded by two waves (8 rows each) through a resource that ends after the
-  // block's last valid row. The block table's entries for 64
-  // consecutive blocks sit one per lane in `tab` and are picked with readlane.
+  // block's last valid row. The blocks are looked up through a window of 64
+  // consecutive logical blocks held one per lane: the element offset of the
+  // block's head-kvh rows in the pool (64-bit), and two masks, `wst` (the
+  // block has storage) and `wok` (it has storage or lies past the sequence,
+  // where position masks its keys anyway). A tile's lookup is then a
+  // readlane and a shift; the window is refilled every 14 tiles, its table
+  // entries loaded one step before they are needed.
   const int rowb = p.Hkv * D * 2;  // bytes between consecutive tokens of one head
-  int tab = -1;
-  int tab_base = -(1 << 30);
-  auto tab_window = [&](int t) {  // entries of blocks 4t-8 .. 4t+3 become readable
-    if (p.table != nullptr && 4 * t + 3 - tab_base >= 64) {
-      tab_base = max(0, 4 * t - 8);
-      const int i = tab_base + lane;
-      tab = i < p.max_blocks ? p.table[(long long)b * p.max_blocks + i] : -1;
-    }
+  int wbase = -(1 << 30);          // first logical block of the window
+  int woff_lo = 0, woff_hi = 0;    // this lane's block offset in elements
+  unsigned long long wst = 0, wok = 0;
+  int nbase = -(1 << 30), nent = -1;  // the next window: first block, this lane's table entry
+  auto fetch = [&](int base) {
+    nbase = base;
+    const int i = base + lane;
+    if (p.table != nullptr)
+      nent = i < p.max_blocks ? p.table[(long long)b * p.max_blocks + i] : -1;
+    else
+      nent = i;
   };
-  // physical block of logical block jb, or -1 when the entry is invalid
-  auto block_of = [&](int jb) -> int {
-    if (p.table == nullptr) return jb;
-    const int e = __builtin_amdgcn_readlane(tab, jb - tab_base);
-    return (e >= 0 && e < p.num_blocks) ? e : -1;
+  auto install = [&]() {
+    wbase = nbase;
+    const int i = wbase + lane;
+    const bool ok = p.table != nullptr ? (nent >= 0 && nent < p.num_blocks) : true;
+    const bool past = nk - kBlockTokens * i <= 0;
+    const long long off =
+        !ok ? 0
+            : p.table != nullptr
+                  ? ((long long)nent * kBlockTokens * p.Hkv + kvh) * D
+                  : (((long long)b * p.max_len + (long long)kBlockTokens * i) * p.Hkv + kvh) * D;
+    woff_lo = (int)(off & 0xffffffffLL);
+    woff_hi = (int)(off >> 32);
+    wst = __builtin_amdgcn_ballot_w64(ok);
+    wok = __builtin_amdgcn_ballot_w64(ok || past);
+  };
+  // make the window cover tile t (called for t = 0, 1, 2, ... in order), and
+  // fetch the next window when tile t+1 would leave this one
+  auto window_for = [&](int t) __attribute__((always_inline)) {
+    if (4 * t + 3 >= wbase + 64) {
+      if (!(nbase <= 4 * t && 4 * t + 3 < nbase + 64)) fetch(max(0, 4 * t - 8));
+      install();
+    }
+    if (4 * t + 7 >= wbase + 64) fetch(max(0, 4 * t - 4));
   };
   auto load_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
     // the waves split the tile's four 16-token blocks evenly: wave w loads
     // rows [16/WB*(w%WB), +16/WB) of block 4t + w/WB, WB = waves per block
     constexpr int WB = kWaves / 4;
     const int jb = 4 * t + wave / WB;
-    const int e = block_of(jb);
+    const int i = jb - wbase;
+    const long long off = ((long long)__builtin_amdgcn_readlane(woff_hi, i) << 32) |
+                          (unsigned)__builtin_amdgcn_readlane(woff_lo, i);
     const int valid = min(kBlockTokens, nk - kBlockTokens * jb);
-    const bool ok = e >= 0 && valid > 0;
-    long long row0 = 0;  // element offset of slot 0 of the block, head kvh
-    if (ok)
-      row0 = p.table == nullptr
-                 ? ((long long)b * p.max_len + (long long)kBlockTokens * jb) * p.Hkv * D + kvh * D
-                 : ((long long)e * kBlockTokens * p.Hkv + kvh) * D;
+    const bool ok = ((wst >> i) & 1ull) != 0 && valid > 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(pool + row0), 0, ok ? (valid - 1) * rowb + D * 2 : 0, kBufferFlags);
+        (void*)(pool + (ok ? off : 0)), 0, ok ? (valid - 1) * rowb + D * 2 : 0, kBufferFlags);
     load_rows(rs, (wave % WB) * (kBlockTokens / WB) * rowb, rowb, dst);
   };
   // bit q: block 4t + q of tile t has storage (blocks past the sequence count
   // as present; their keys are masked by position)
   auto tile_ok_bits = [&](int t) -> unsigned {
-    unsigned bits = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int jb = 4 * t + q;
-      const bool ok = nk - kBlockTokens * jb <= 0 || block_of(jb) >= 0;
-      bits |= (ok ? 1u : 0u) << q;
-    }
-    return bits;
+    return (unsigned)(wok >> (4 * t - wbase)) & 0xFu;
   };
   // tile t's K, V into LDS; issue_k returns the tile's block bits (cache)
   auto issue_k = [&](int t, char* dst) __attribute__((always_inline)) -> unsigned {
     if constexpr (CACHE) {
-      tab_window(t);
+      window_for(t);
       load_block(p.k, t, dst);
       return tile_ok_bits(t);
     } else {

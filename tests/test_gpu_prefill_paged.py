@@ -74,15 +74,21 @@ def test_contiguous_chunk(B, Hq, Hkv, Nq, d, L, lens):
     check(o, O, lse, Lr, "bf16", "contiguous-cache prefill")
 
 
-def test_invalid_table_entries_hide_their_keys():
+@pytest.mark.parametrize("cached,hidden", [
+    (150, ((0, 2), (1, 7))),
+    # past the first 64 blocks of a sequence, and at the 64-block boundary
+    (1400, ((0, 63), (0, 64), (1, 70))),
+])
+def test_invalid_table_entries_hide_their_keys(cached, hidden):
     dev = need_gpu()
-    announce("paged prefill with -1 / out-of-range table entries, B=2 Hq=4 Hkv=1 Nq=40 d=128")
-    inp = inputs.paged_inputs(33, 2, 4, 1, 40, 128, 150, 150, spare_blocks=0)
+    announce(f"paged prefill with -1 / out-of-range table entries {hidden}, B=2 Hq=4 Hkv=1 Nq=40 "
+             f"d=128 cached={cached}")
+    inp = inputs.paged_inputs(33, 2, 4, 1, 40, 128, cached, cached, spare_blocks=0)
     kp = oracle.kv_append_ref(inp["k_pool"], inp["k_new"], inp["block_table"], inp["cache_lens"])
     vp = oracle.kv_append_ref(inp["v_pool"], inp["v_new"], inp["block_table"], inp["cache_lens"])
     table = inp["block_table"].clone()
-    table[0, 2] = -1
-    table[1, 7] = inp["num_blocks"] + 3
+    for i, (b, blk) in enumerate(hidden):
+        table[b, blk] = -1 if i % 2 == 0 else inp["num_blocks"] + 3
     o, lse = eta.attn_prefill_paged(inp["q"].to(dev), kp.to(dev), vp.to(dev),
                                     inp["seq_lens"].to(dev), block_table=table.to(dev),
                                     causal=True)
@@ -91,9 +97,10 @@ def test_invalid_table_entries_hide_their_keys():
     Nq = 40
     O = np.zeros((2, Nq, 4, 128))
     L = np.zeros((2, 4, Nq))
-    for b, hide in ((0, 2), (1, 7)):
+    for b in (0, 1):
         n = int(inp["seq_lens"][b])
-        keep = [t for t in range(n) if t // 16 != hide]
+        hide = {blk for bb, blk in hidden if bb == b}
+        keep = [t for t in range(n) if t // 16 not in hide]
         K = oracle.gather_paged(kp, inp["block_table"][b], n)
         V = oracle.gather_paged(vp, inp["block_table"][b], n)
         for hq in range(4):
