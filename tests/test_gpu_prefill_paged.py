@@ -63,6 +63,7 @@ def test_paged_chunk(B, Hq, Hkv, Nq, d, lo, hi, causal):
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,d,L,lens", [
     (2, 8, 2, 70, 128, 400, [400, 70]),
     (3, 8, 8, 33, 64, 200, [200, 33, 150]),
+    (2, 8, 2, 70, 128, 1600, [1537, 1100]),  # more than 64 blocks of 16 tokens
 ])
 def test_contiguous_chunk(B, Hq, Hkv, Nq, d, L, lens):
     dev = need_gpu()
