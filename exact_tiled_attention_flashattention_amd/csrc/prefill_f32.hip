@@ -7,11 +7,11 @@
 // loads and a chain of dependent arithmetic per row. So the work is spread
 // thin. A workgroup owns 16 query rows of one head (4 lanes per row, each
 // holding a quarter of q and of the output in interleaved 16-byte chunks)
-// and its 4 waves take every fourth tile of keys each, so a row's chain of
-// keys is split four ways. Each wave streams its own tiles through a private
+// and its 16 waves take every 16th tile of keys each, so a row's chain of
+// keys is split 16 ways. Each wave streams its own tiles through a private
 // double buffer in LDS with direct global->LDS loads (no workgroup barrier
 // inside the loop), runs the running (max, sum) update over them, and at the
-// end the four partial results of each row are merged through LDS with the
+// end the 16 partial results of each row are merged through LDS with the
 // same log-sum-exp weights as the split-KV decode.
 #include "common.h"
 #include "launch.h"
@@ -20,7 +20,7 @@ namespace attn {
 namespace {
 
 constexpr int kRows = 16;    // query rows per workgroup
-constexpr int kWaves = 4;    // key-parallel waves per workgroup
+constexpr int kWaves = 16;   // key-parallel waves per workgroup
 constexpr int kBufferFlags = 0x00020000;
 
 struct F32Params {
@@ -36,9 +36,9 @@ struct F32Params {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_f32_kernel(F32Params p) {
+__global__ __launch_bounds__(kWaves * 64) void prefill_f32_kernel(F32Params p) {
   constexpr int NE = D / 16;       // float4 chunks per lane
-  constexpr int TK = 2048 / D;     // keys per staged tile (8 KiB of K, 8 KiB of V)
+  constexpr int TK = 512 / D;      // keys per staged tile (2 KiB of K, 2 KiB of V)
   constexpr int TILEF = TK * D;    // floats per K (or V) tile
   constexpr int NL = TILEF / 256;  // 16-byte direct loads per lane per tile and tensor
   // per wave: [buffer 0: K, V][buffer 1: K, V]; reused for the final merge
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Params p) {
     buf ^= 1;
   }
 
-  // ---- merge the four waves' partial results of each row -----------------------
+  // ---- merge the waves' partial results of each row ----------------------------
   // O = Σ_w 2^(m_w − M) O_w / Σ_w 2^(m_w − M) l_w with M = max_w m_w (an
   // empty partial has m_w = −inf and weight 0)
   __syncthreads();  // every wave is done with its tiles: the buffers become the merge area
@@ -226,9 +226,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.d == 128)
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((int)nblocks), dim3(256), 0, s, pp);
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((int)nblocks), dim3(kWaves * 64), 0, s, pp);
   else
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((int)nblocks), dim3(256), 0, s, pp);
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((int)nblocks), dim3(kWaves * 64), 0, s, pp);
   return hipGetLastError();
 }
 
