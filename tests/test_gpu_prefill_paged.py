@@ -48,6 +48,7 @@ def _append_and_run(inp, dev, causal=True):
     (1, 8, 1, 130, 64, 33, 33, False),      # G=8, not causal
     (2, 6, 3, 48, 128, 10, 100, True),      # G=2
     (1, 32, 8, 600, 128, 0, 0, True),       # first chunk: plain causal prefill through the cache
+    (70, 4, 2, 4, 64, 1, 120, True),        # more sequences than lanes: launch order by index
 ])
 def test_paged_chunk(B, Hq, Hkv, Nq, d, lo, hi, causal):
     dev = need_gpu()
