@@ -8,13 +8,14 @@
 // the output once. Scores and probabilities live only in registers.
 //
 // Mapping onto CDNA4:
-//   * A workgroup is 8 waves. The waves share one K/V head: with a group of
+//   * A workgroup is 8 waves (4 for launches with fewer than two 8-wave
+//     workgroups per CU). The waves share one K/V head: with a group of
 //     G = Hq/Hkv query heads ("Effizienz", "GQA im leicht lesbaren Code")
-//     they take 4 heads of the group at 64 positions (G % 4 == 0), else
+//     they take 4 heads of the group at 64 (32) positions (G % 4 == 0), else
 //     fewer heads at more positions. Every K/V tile is read from HBM/L2 once
-//     per workgroup and used by all its waves. One workgroup fills a CU (two
-//     waves per SIMD), and the two waves sharing a SIMD step through the same
-//     tiles between the same barriers, so they progress at the same rate.
+//     per workgroup and used by all its waves. An 8-wave workgroup fills a CU
+//     (two waves per SIMD), and the two waves sharing a SIMD step through the
+//     same tiles between the same barriers, so they progress at the same rate.
 //   * Each wave owns 32 query rows. Scores are computed transposed,
 //     Sᵀ = K·Qᵀ, with v_mfma_f32_32x32x16_bf16 (K from LDS as the A
 //     operand, Qᵀ held in registers as the B operand), so each lane holds
@@ -39,7 +40,6 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 8;  // waves per workgroup: one workgroup fills a CU
 constexpr int kBN = 64;         // keys per tile
 constexpr float kTau = 8.0f;    // rescale only when a row max grows by more than 2^8
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, 32-bit dword data
@@ -85,7 +85,9 @@ __device__ __forceinline__ int lds_off(int row, int elem) {  // byte offset of e
   return row * (D * 2) + ((((elem >> 3) ^ swz<D>(row))) << 4) + ((elem & 7) << 1);
 }
 
-template <int D, bool CAUSAL, bool CACHE>
+// kWaves waves per workgroup: 8 (one workgroup fills a CU) or 4 (two share
+// one) -- see launch_prefill_bf16
+template <int D, bool CAUSAL, bool CACHE, int kWaves>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves),
                           amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(PrefillParams p) {
@@ -508,21 +510,20 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool CACHE>
+template <int D, bool CAUSAL, bool CACHE, int W>
 hipError_t launch_typed(const PrefillParams& pp, int nblocks, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, CACHE>), dim3(nblocks),
-                     dim3(kWaves * 64), 0,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, CACHE, W>), dim3(nblocks), dim3(W * 64), 0,
                      s, pp);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int W>
 hipError_t launch_d(const PrefillParams& pp, bool causal, bool cache, int nblocks, hipStream_t s) {
   if (cache)
-    return causal ? launch_typed<D, true, true>(pp, nblocks, s)
-                  : launch_typed<D, false, true>(pp, nblocks, s);
-  return causal ? launch_typed<D, true, false>(pp, nblocks, s)
-                : launch_typed<D, false, false>(pp, nblocks, s);
+    return causal ? launch_typed<D, true, true, W>(pp, nblocks, s)
+                  : launch_typed<D, false, true, W>(pp, nblocks, s);
+  return causal ? launch_typed<D, true, false, W>(pp, nblocks, s)
+                : launch_typed<D, false, false, W>(pp, nblocks, s);
 }
 
 }  // namespace
@@ -541,9 +542,16 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   pp.Nk = a.Nk;
   pp.G = a.Hq / a.Hkv;
   pp.hw = (pp.G % 4 == 0) ? 4 : ((pp.G % 2 == 0) ? 2 : 1);
-  pp.pw = kWaves / pp.hw;
-  pp.n_qblk = (a.Nq + 32 * pp.pw - 1) / (32 * pp.pw);
   pp.n_hgrp = pp.G / pp.hw;
+  // 8-wave workgroups (the two waves on a SIMD step through the same tiles)
+  // when there are at least two per CU; fewer, and a CU's one workgroup
+  // could not be paired with a shorter one, so two 4-wave workgroups share
+  // each CU instead (a causal prefill of 2048 rows: 49 against 58 us)
+  const long long per_row_block = (long long)a.B * a.Hkv * pp.n_hgrp;
+  const long long nq8 = (a.Nq + 32 * (8 / pp.hw) - 1) / (32 * (8 / pp.hw));
+  const int W = nq8 * per_row_block >= 2LL * device_compute_units() ? 8 : 4;
+  pp.pw = W / pp.hw;
+  pp.n_qblk = (a.Nq + 32 * pp.pw - 1) / (32 * pp.pw);
   pp.c = a.scale * kLog2e;
   pp.q_offset = a.q_offset;
   const long long d = a.d;
@@ -565,8 +573,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const bool cache = a.cache != 0;
-  if (a.d == 128) return launch_d<128>(pp, a.causal, cache, (int)nblocks, s);
-  return launch_d<64>(pp, a.causal, cache, (int)nblocks, s);
+  if (W == 8)
+    return a.d == 128 ? launch_d<128, 8>(pp, a.causal, cache, (int)nblocks, s)
+                      : launch_d<64, 8>(pp, a.causal, cache, (int)nblocks, s);
+  return a.d == 128 ? launch_d<128, 4>(pp, a.causal, cache, (int)nblocks, s)
+                    : launch_d<64, 4>(pp, a.causal, cache, (int)nblocks, s);
 }
 
 }  // namespace attn
