@@ -544,12 +544,15 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   pp.hw = (pp.G % 4 == 0) ? 4 : ((pp.G % 2 == 0) ? 2 : 1);
   pp.n_hgrp = pp.G / pp.hw;
   // 8-wave workgroups (the two waves on a SIMD step through the same tiles)
-  // when there are at least two per CU; fewer, and a CU's one workgroup
-  // could not be paired with a shorter one, so two 4-wave workgroups share
-  // each CU instead (a causal prefill of 2048 rows: 49 against 58 us)
+  // when they fill the chip: one per CU at least, and under a causal mask
+  // (workgroups of unequal length) two per CU, so that long and short ones
+  // can follow each other. Otherwise two 4-wave workgroups share each CU (a
+  // causal prefill of 2048 rows: 49 against 58 us; a non-causal one of 1024
+  // rows: 27-30 against 36 us).
   const long long per_row_block = (long long)a.B * a.Hkv * pp.n_hgrp;
   const long long nq8 = (a.Nq + 32 * (8 / pp.hw) - 1) / (32 * (8 / pp.hw));
-  const int W = nq8 * per_row_block >= 2LL * device_compute_units() ? 8 : 4;
+  const long long need8 = (long long)device_compute_units() * (a.causal ? 2 : 1);
+  const int W = nq8 * per_row_block >= need8 ? 8 : 4;
   pp.pw = W / pp.hw;
   pp.n_qblk = (a.Nq + 32 * pp.pw - 1) / (32 * pp.pw);
   pp.c = a.scale * kLog2e;
