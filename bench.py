@@ -477,12 +477,12 @@ def main():
     torch.cuda.synchronize()
     result_workloads["single_head_f32"] = {"us": round(t1.mean_ms("p") * 1e3, 2)}
 
-    traffic = counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true,false>",
+    traffic = counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true,false,8>",
                               ["common.h", "prefill_bf16.hip"])
     roofline = {"bound": "mfma", "achieved": round(tflops2, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tflops2 / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "traffic_unit": "bytes per launch (HBM read + write)",
-                "kernel": "prefill_bf16_kernel<128, causal, slabs>",
+                "kernel": "prefill_bf16_kernel<128, true, false, 8>",
                 "per_launch": f"{flops2:.6g} FLOP (visible pairs x 4d) per launch"}
 
     if not args.no_chat_sim:
