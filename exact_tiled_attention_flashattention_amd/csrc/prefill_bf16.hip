@@ -490,19 +490,43 @@ void prefill_bf16_kernel(PrefillParams p) {
   }
 
   // ---- epilogue: O = Oᵀ/l written once, LSE = ln(sum) + max --------------------
+  // A lane holds 8-byte pieces of its row; written straight out, every store
+  // would touch 32 rows. The wave's 32 rows therefore pass through LDS (its
+  // own 32 rows of the tile buffers, free once every wave is past its last
+  // tile: the barrier below) and leave as whole rows, 16 bytes per lane.
   const float l_tot = sum_across_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  constexpr int RB = D * 2;    // bytes per row
+  constexpr int NCH = D / 8;   // 16-byte chunks per row; chunk c of row r sits at c ^ (r % NCH)
+  char* stage = ((wave >> 1) == 0 ? kb0 : (wave >> 1) == 1 ? kb1 : (wave >> 1) == 2 ? vb0 : vb1) +
+                (wave & 1) * 32 * RB;
+  static_assert(2 * 32 * RB == TILE, "two waves' rows fill one tile buffer");
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      f32x4_t v4 = {acc[db][4 * ii] * inv, acc[db][4 * ii + 1] * inv, acc[db][4 * ii + 2] * inv,
+                    acc[db][4 * ii + 3] * inv};
+      const int c = 4 * db + ii;
+      *reinterpret_cast<bf16x4_t*>(stage + l32 * RB + ((c ^ (l32 & (NCH - 1))) << 4) + 8 * g) =
+          __builtin_convertvector(v4, bf16x4_t);
+    }
+  __syncthreads();
+  {
+    const int row0 = q0 + sub * 32;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const int r = i * (64 / NCH) + lane / NCH;
+      const int c = lane % NCH;
+      const u32x4_t val =
+          *reinterpret_cast<const u32x4_t*>(stage + r * RB + ((c ^ (r & (NCH - 1))) << 4));
+      if (row0 + r < p.Nq)
+        *reinterpret_cast<u32x4_t*>(p.o + b * p.sqb + hq * p.sqh + (row0 + r) * p.sqr + 8 * c) =
+            val;
+    }
+  }
   if (my_q < p.Nq) {
-    __bf16* op = p.o + b * p.sqb + hq * p.sqh + my_q * p.sqr;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        f32x4_t v4 = {acc[db][4 * ii] * inv, acc[db][4 * ii + 1] * inv, acc[db][4 * ii + 2] * inv,
-                      acc[db][4 * ii + 3] * inv};
-        *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * ii + 4 * g) =
-            __builtin_convertvector(v4, bf16x4_t);
-      }
     if (g == 0 && p.lse != nullptr) {
       p.lse[((long long)b * p.Hq + hq) * p.Nq + my_q] =
           l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : neg_inf();
