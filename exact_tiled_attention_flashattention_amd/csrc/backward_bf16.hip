@@ -300,17 +300,35 @@ void bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  if (row_ok) {
-    __bf16* op = p.dq + ((long long)b * p.Hq + hq) * p.Nq * D + (long long)my_q * D;
+  // dQ rows pass through the wave's own 32 rows of the (then free) tile
+  // buffers, so that each store writes whole rows, 16 bytes per lane, instead
+  // of 8-byte pieces of 32 rows
+  constexpr int RB = D * 2;    // bytes per row
+  constexpr int NCH = D / 8;   // 16-byte chunks per row; chunk c of row r sits at c ^ (r % NCH)
+  static_assert(2 * 32 * RB == TILE, "two waves' rows fill one tile buffer");
+  char* stage = ((wave >> 1) == 0 ? kb0 : vb0) + (wave & 1) * 32 * RB;
+  __syncthreads();
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        f32x4_t v4 = {acc[db][4 * ii] * p.scale, acc[db][4 * ii + 1] * p.scale,
-                      acc[db][4 * ii + 2] * p.scale, acc[db][4 * ii + 3] * p.scale};
-        *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * ii + 4 * g) =
-            __builtin_convertvector(v4, bf16x4_t);
-      }
+    for (int ii = 0; ii < 4; ++ii) {
+      f32x4_t v4 = {acc[db][4 * ii] * p.scale, acc[db][4 * ii + 1] * p.scale,
+                    acc[db][4 * ii + 2] * p.scale, acc[db][4 * ii + 3] * p.scale};
+      const int c = 4 * db + ii;
+      *reinterpret_cast<bf16x4_t*>(stage + l32 * RB + ((c ^ (l32 & (NCH - 1))) << 4) + 8 * g) =
+          __builtin_convertvector(v4, bf16x4_t);
+    }
+  __syncthreads();
+  const int row0 = q0 + sub * 32;
+  __bf16* const dq_head = p.dq + ((long long)b * p.Hq + hq) * p.Nq * D;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) {
+    const int r = i * (64 / NCH) + lane / NCH;
+    const int c = lane % NCH;
+    const u32x4_t val =
+        *reinterpret_cast<const u32x4_t*>(stage + r * RB + ((c ^ (r & (NCH - 1))) << 4));
+    if (row0 + r < p.Nq)
+      *reinterpret_cast<u32x4_t*>(dq_head + (long long)(row0 + r) * D + 8 * c) = val;
   }
 }
 
