@@ -527,24 +527,58 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  if (my_key < p.Nk) {
-    const long long off = kv_base + (long long)my_key * D;
-    const long long plane = (long long)p.B * p.Hkv * p.Nk * D;
-    const float f = role == 0 ? 1.f : p.scale;
-    __bf16* out = role == 0 ? p.dv : p.dk;
-    float* part = p.part + ((role == 0 ? p.nsplit : 0) + split) * plane + off;
+  // The slice's 32 rows pass through LDS (a region of the then free tile and
+  // P buffers per wave) so that each store writes whole rows, 16 bytes per
+  // lane, instead of pieces of 32 rows: bf16 rows when the workgroup owns the
+  // whole sum, fp32 partial rows otherwise.
+  static_assert(sizeof(pbuf) >= 2 * TILE && 32 * D * 4 == TILE, "eight regions of 32 fp32 rows");
+  char* const stage = wave8 < 3   ? qbuf[wave8]
+                      : wave8 < 6 ? obuf[wave8 - 3]
+                                  : reinterpret_cast<char*>(pbuf) + (wave8 - 6) * TILE;
+  const float f = role == 0 ? 1.f : p.scale;
+  const bool whole = p.nsplit == 1;
+  constexpr int RB = D * 2, NCH = D / 8;    // bf16 rows: bytes, 16-byte chunks
+  constexpr int RF = D * 4, NCF = D / 4;    // fp32 rows
+  __syncthreads();
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        f32x4_t v4 = {acc[db][4 * ii] * f, acc[db][4 * ii + 1] * f, acc[db][4 * ii + 2] * f,
-                      acc[db][4 * ii + 3] * f};
-        const int e = 32 * db + 8 * ii + 4 * g;
-        if (p.nsplit == 1)
-          *reinterpret_cast<bf16x4_t*>(out + off + e) = __builtin_convertvector(v4, bf16x4_t);
-        else
-          *reinterpret_cast<f32x4_t*>(part + e) = v4;
+    for (int ii = 0; ii < 4; ++ii) {
+      f32x4_t v4 = {acc[db][4 * ii] * f, acc[db][4 * ii + 1] * f, acc[db][4 * ii + 2] * f,
+                    acc[db][4 * ii + 3] * f};
+      if (whole) {
+        const int c = 4 * db + ii;
+        *reinterpret_cast<bf16x4_t*>(stage + l32 * RB + ((c ^ (l32 & (NCH - 1))) << 4) + 8 * g) =
+            __builtin_convertvector(v4, bf16x4_t);
+      } else {
+        const int c = 8 * db + 2 * ii + g;
+        *reinterpret_cast<f32x4_t*>(stage + l32 * RF + ((c ^ (l32 & (NCF - 1))) << 4)) = v4;
       }
+    }
+  __syncthreads();
+  const long long plane = (long long)p.B * p.Hkv * p.Nk * D;
+  if (whole) {
+    __bf16* const out = (role == 0 ? p.dv : p.dk) + kv_base;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {
+      const int r = i * (64 / NCH) + lane / NCH;
+      const int c = lane % NCH;
+      const u32x4_t val =
+          *reinterpret_cast<const u32x4_t*>(stage + r * RB + ((c ^ (r & (NCH - 1))) << 4));
+      if (kw0 + r < p.Nk)
+        *reinterpret_cast<u32x4_t*>(out + (long long)(kw0 + r) * D + 8 * c) = val;
+    }
+  } else {
+    float* const part = p.part + ((role == 0 ? p.nsplit : 0) + split) * plane + kv_base;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      const int r = i * (64 / NCF) + lane / NCF;
+      const int c = lane % NCF;
+      const f32x4_t val =
+          *reinterpret_cast<const f32x4_t*>(stage + r * RF + ((c ^ (r & (NCF - 1))) << 4));
+      if (kw0 + r < p.Nk)
+        *reinterpret_cast<f32x4_t*>(part + (long long)(kw0 + r) * D + 4 * c) = val;
+    }
   }
 }
 
