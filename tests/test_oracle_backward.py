@@ -9,6 +9,8 @@ forms (one key; equal values), exact identities of the softmax Jacobian
 to the visible rows' dO), the causal horizon, and the GQA sum over a group.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -173,6 +175,83 @@ def test_magnitudes_bound_the_gradients():
     assert (mk[:, :, 33:] == 0).all() and (mv[:, :, 33:] == 0).all()  # keys no row sees
 
 
+def _brute_magnitudes(q, pos, k, v, do, scale, causal):
+    """Every gradient element as an explicit list of its terms, with Python
+    floats and math.exp; the magnitude is the sum of the terms' absolute
+    values. dV_jc = Σ_i P_ij dO_ic; dQ_ic = scale Σ_j dS_ij K_jc and
+    dK_jc = scale Σ_i dS_ij Q_ic, each term widened by P_ij E_i with
+    E_i = Σ_c |dO_ic| |O_ic| (the size of the terms of D_i = dO_i · O_i)."""
+    R, d = len(q), len(q[0])
+    n, dv_ = len(k), len(v[0])
+    vis = [[(not causal) or j <= pos[i] for j in range(n)] for i in range(R)]
+    P = []
+    for i in range(R):
+        s = [scale * sum(q[i][c] * k[j][c] for c in range(d)) for j in range(n)]
+        seen = [s[j] for j in range(n) if vis[i][j]]
+        if not seen:
+            P.append([0.0] * n)
+            continue
+        mx = max(seen)
+        e = [math.exp(s[j] - mx) if vis[i][j] else 0.0 for j in range(n)]
+        tot = sum(e)
+        P.append([x / tot for x in e])
+    O = [[sum(P[i][j] * v[j][c] for j in range(n)) for c in range(dv_)] for i in range(R)]
+    dP = [[sum(do[i][c] * v[j][c] for c in range(dv_)) for j in range(n)] for i in range(R)]
+    D = [sum(P[i][j] * dP[i][j] for j in range(n)) for i in range(R)]
+    dS = [[P[i][j] * (dP[i][j] - D[i]) for j in range(n)] for i in range(R)]
+    E = [sum(abs(do[i][c]) * abs(O[i][c]) for c in range(dv_)) for i in range(R)]
+    mv = [[sum(abs(P[i][j] * do[i][c]) for i in range(R)) for c in range(dv_)] for j in range(n)]
+    mq = [[sum(abs(scale * dS[i][j] * k[j][c]) + scale * P[i][j] * E[i] * abs(k[j][c])
+               for j in range(n)) for c in range(d)] for i in range(R)]
+    mk = [[sum(abs(scale * dS[i][j] * q[i][c]) + scale * P[i][j] * E[i] * abs(q[i][c])
+               for i in range(R)) for c in range(d)] for j in range(n)]
+    return np.array(mq), np.array(mk), np.array(mv)
+
+
+@pytest.mark.parametrize("causal,off", [(False, 0), (True, 1), (True, -1)])
+def test_magnitudes_brute_force(causal, off):
+    # exact from both sides: an inflated or deflated magnitude fails
+    rng = np.random.default_rng(21)
+    R, n, d = 4, 5, 3
+    q, k, v, do = (_rand(rng, R, d), _rand(rng, n, d), _rand(rng, n, d), _rand(rng, R, d))
+    pos = np.arange(R) + off
+    *_, (mq, mk, mv) = ob.attention_backward_rows(q, pos, k, v, do, 0.7, causal, magnitudes=True)
+    bq, bk, bv = _brute_magnitudes(q.tolist(), pos.tolist(), k.tolist(), v.tolist(),
+                                   do.tolist(), 0.7, causal)
+    for got, ref in ((mq, bq), (mk, bk), (mv, bv)):
+        assert np.abs(got - ref).max() <= 1e-13 * max(1.0, np.abs(ref).max())
+
+
+def test_magnitudes_one_key_closed_form():
+    # one key: P = 1, O_i = V_0 and dS = 0, so every magnitude is a closed form:
+    # Mv_0 = Σ_i |dO_i|, Mq_i = scale E_i |K_0|, Mk_0 = scale Σ_i E_i |Q_i| with
+    # E_i = Σ_c |dO_ic| |V_0c|
+    rng = np.random.default_rng(22)
+    R, d, scale = 6, 4, 0.3
+    q, k, v, do = (_rand(rng, R, d), _rand(rng, 1, d), _rand(rng, 1, d), _rand(rng, R, d))
+    *_, (mq, mk, mv) = ob.attention_backward_rows(q, np.arange(R), k, v, do, scale, False,
+                                                  magnitudes=True)
+    E = np.abs(do) @ np.abs(v[0])
+    assert np.allclose(mv[0], np.abs(do).sum(axis=0), rtol=1e-14, atol=0)
+    assert np.allclose(mq, scale * E[:, None] * np.abs(k[0])[None, :], rtol=1e-14, atol=0)
+    assert np.allclose(mk[0], scale * (E[:, None] * np.abs(q)).sum(axis=0), rtol=1e-14, atol=0)
+
+
+def test_magnitudes_equal_the_gradient_when_terms_share_a_sign():
+    # dO >= 0: every term of dV_jc = Σ_i P_ij dO_ic is >= 0, so Mv equals dV
+    rng = np.random.default_rng(23)
+    R, n, d = 7, 9, 5
+    q, k, v = _rand(rng, R, d), _rand(rng, n, d), _rand(rng, n, d)
+    do = np.abs(_rand(rng, R, d))
+    dq, dk, dv, (mq, mk, mv) = ob.attention_backward_rows(q, np.arange(R) + 2, k, v, do, 0.5,
+                                                          True, magnitudes=True)
+    assert np.allclose(mv, dv, rtol=1e-13, atol=0)
+    # V = 0: O = 0 and dP = 0, so dS = 0, E = 0 and Mq = Mk = 0 exactly
+    *_, (mq0, mk0, _) = ob.attention_backward_rows(q, np.arange(R), k, 0 * v, do, 0.5, True,
+                                                   magnitudes=True)
+    assert (mq0 == 0).all() and (mk0 == 0).all()
+
+
 def test_kv_head_sample_matches_full():
     rng = np.random.default_rng(9)
     q = _rand(rng, 2, 4, 9, 4)
@@ -222,6 +301,36 @@ def test_planted_mistake_is_caught(monkeypatch, what, old, new):
     pins = [lambda: test_matches_torch_autograd(True, 37),
             lambda: test_matches_torch_autograd(False, 0),
             lambda: test_finite_differences(True, 3, 3)]
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"no pin caught: {what}"
+
+
+MAG_MUTANTS = [
+    ("W inflated x10", "W = np.abs(dS) + P * Ei[:, None]", "W = 10.0 * (np.abs(dS) + P * Ei[:, None])"),
+    ("Mv inflated x4", "mv += P.T @ np.abs(dout[r0:r1])", "mv += 4.0 * (P.T @ np.abs(dout[r0:r1]))"),
+    ("Mq inflated x2", "mq[r0:r1] = scale * (W @ np.abs(k))", "mq[r0:r1] = 2.0 * scale * (W @ np.abs(k))"),
+    ("Mk inflated x2", "mk += scale * (W.T @ np.abs(q[r0:r1]))",
+     "mk += 2.0 * scale * (W.T @ np.abs(q[r0:r1]))"),
+    ("E term dropped", "W = np.abs(dS) + P * Ei[:, None]", "W = np.abs(dS)"),
+    ("E from |V| not |O|", "Ei = (np.abs(dout[r0:r1]) * np.abs(P @ v)).sum(axis=1)",
+     "Ei = (np.abs(dout[r0:r1]) * (P @ np.abs(v))).sum(axis=1)"),
+    ("|dS| replaced by dS", "W = np.abs(dS) + P * Ei[:, None]", "W = dS + P * Ei[:, None]"),
+]
+
+
+@pytest.mark.parametrize("what,old,new", MAG_MUTANTS, ids=[m[0] for m in MAG_MUTANTS])
+def test_planted_magnitude_mistake_is_caught(monkeypatch, what, old, new):
+    mod = _mutant(old, new)
+    monkeypatch.setattr(ob, "attention_backward_rows", mod.attention_backward_rows)
+    monkeypatch.setattr(ob, "prefill_backward", mod.prefill_backward)
+    pins = [lambda: test_magnitudes_brute_force(True, 1),
+            lambda: test_magnitudes_one_key_closed_form(),
+            lambda: test_magnitudes_equal_the_gradient_when_terms_share_a_sign()]
     failed = 0
     for pin in pins:
         try:
