@@ -123,6 +123,7 @@ def _check(status, where):
 
 
 def _need_gpu(*ts):
+    dev = None
     for t in ts:
         if t is None:
             continue
@@ -130,26 +131,49 @@ def _need_gpu(*ts):
             raise ValueError("tensors must be on a GPU device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors must share one device ({dev} and {t.device})")
+
+
+def _dims(t, n, name):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {list(t.shape)}")
+    return tuple(t.shape)
+
+
+def _expect(t, shape, dtype, name):
+    """A caller-supplied output (or input) must have exactly this shape and dtype:
+    the kernels write and read it with that layout and nothing else bounds them."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
 def attn_prefill(q, k, v, scale=None, causal=False, q_offset=0, out=None, lse=None,
                  want_lse=True):
     """Prefill. q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d] -> o [B,Hq,Nq,d], lse [B,Hq,Nq] f32."""
     lib = _load()
-    _need_gpu(q, k, v)
-    B, Hq, Nq, d = q.shape
+    B, Hq, Nq, d = _dims(q, 4, "q")
+    _dims(k, 4, "k")
     Hkv, Nk = k.shape[1], k.shape[2]
     if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse")
+    _need_gpu(q, k, v, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    _need_gpu(out, lse)
     st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq,
                           Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(q_offset),
                           _stream(q.device))
@@ -162,8 +186,8 @@ def attn_prefill_backward(q, k, v, o, lse, dout, scale=None, causal=False, q_off
     """Backward of attn_prefill (bf16). q, o, dout [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d];
     lse [B,Hq,Nq] f32 from the forward -> dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d]."""
     lib = _load()
-    _need_gpu(q, k, v, o, lse, dout)
-    B, Hq, Nq, d = q.shape
+    B, Hq, Nq, d = _dims(q, 4, "q")
+    _dims(k, 4, "k")
     Hkv, Nk = k.shape[1], k.shape[2]
     if k.shape != (B, Hkv, Nk, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, Hkv, Nk, d] matching q")
@@ -174,6 +198,10 @@ def attn_prefill_backward(q, k, v, o, lse, dout, scale=None, causal=False, q_off
             raise TypeError("q, k, v, o, dout must share one dtype")
     if lse.dtype != torch.float32 or lse.shape != (B, Hq, Nq):
         raise ValueError("lse must be float32 [B, Hq, Nq]")
+    _expect(dq, q.shape, q.dtype, "dq")
+    _expect(dk, k.shape, q.dtype, "dk")
+    _expect(dv, v.shape, q.dtype, "dv")
+    _need_gpu(q, k, v, o, lse, dout, dq, dk, dv, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if dq is None:
@@ -186,7 +214,6 @@ def attn_prefill_backward(q, k, v, o, lse, dout, scale=None, causal=False, q_off
                                                          int(q_offset)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _need_gpu(dq, dk, dv, workspace)
     st = lib.attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _dtype_code(q), B, Hq, Hkv, Nq,
                                    Nk, d, float(scale), int(bool(causal)), int(q_offset),
@@ -201,11 +228,17 @@ def attn_prefill_backward_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal=False, q
                                                              int(bool(causal)), int(q_offset)))
 
 
-def _check_cache_args(q, k_cache, v_cache, seq_lens, block_table):
-    B, Nq, Hq, d = q.shape
+def _check_cache_args(q, k_cache, v_cache, seq_lens, block_table, fp8=False):
+    B, Nq, Hq, d = _dims(q, 4, "q")
+    _dims(k_cache, 4, "k_cache")
     if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache/v_cache must share a shape with head dim d")
-    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+    if fp8:
+        if q.dtype != torch.bfloat16:
+            raise TypeError("q is bf16")
+        _fp8_cache(k_cache)
+        _fp8_cache(v_cache)
+    elif k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q and the caches must share one dtype")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be int32 [B]")
@@ -224,18 +257,19 @@ def attn_prefill_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=No
     [B,L,Hkv,d] (contiguous); seq_lens [B] int32 (keys incl. the Nq new ones)
     -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
     lib = _load()
-    _need_gpu(q, k_cache, v_cache, seq_lens, block_table)
     _check_cache_args(q, k_cache, v_cache, seq_lens, block_table)
     B, Nq, Hq, d = q.shape
     Hkv = k_cache.shape[2]
     L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse")
+    _need_gpu(q, k_cache, v_cache, seq_lens, block_table, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    _need_gpu(out, lse)
     st = lib.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), mb,
                                 nblocks, _ptr(seq_lens), _ptr(out), _ptr(lse), _dtype_code(q), B,
                                 Hq, Hkv, Nq, d, float(scale), int(bool(causal)), L,
@@ -254,12 +288,31 @@ def attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, max_seq_len, num_splits=0):
     return int(_load().attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, max_seq_len, num_splits))
 
 
+def _check_table(block_table, cache, B):
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be int32 [B, max_blocks]")
+        if cache.shape[1] != BLOCK_TOKENS:
+            raise ValueError("a paged cache is [num_blocks, 16, Hkv, d]")
+    elif cache.shape[0] != B:
+        raise ValueError("a contiguous cache is [B, max_len, Hkv, d]")
+
+
 def _cache_geometry(k_cache, block_table, max_seq_len):
+    """(max_len, max_blocks_per_seq, num_blocks) of a cache. A contiguous cache's
+    max_len is its row stride ([B, max_len, Hkv, d]), so it must be the tensor's
+    own second dimension; a paged cache's max_len only caps the positions."""
     if block_table is None:
         cap = k_cache.shape[1]
-        return (cap if max_seq_len is None else int(max_seq_len)), 0, 0
+        if max_seq_len is not None and int(max_seq_len) != cap:
+            raise ValueError(f"a contiguous cache's max_seq_len is its second dimension ({cap}), "
+                             f"got {max_seq_len}")
+        return cap, 0, 0
     mb = block_table.shape[1]
     cap = mb * BLOCK_TOKENS
+    if max_seq_len is not None and not 0 <= int(max_seq_len) <= cap:
+        raise ValueError(f"max_seq_len must be in [0, {cap}] (16 x the table's columns), "
+                         f"got {max_seq_len}")
     return (cap if max_seq_len is None else int(max_seq_len)), mb, k_cache.shape[0]
 
 
@@ -269,21 +322,13 @@ def attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=Non
     """Decode. q [B,Nq,Hq,d]; caches [P,16,Hkv,d] (paged) or [B,L,Hkv,d] (contiguous);
     seq_lens [B] int32 (keys incl. the Nq new ones) -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
     lib = _load()
-    _need_gpu(q, k_cache, v_cache, seq_lens, block_table)
+    _check_cache_args(q, k_cache, v_cache, seq_lens, block_table)
     B, Nq, Hq, d = q.shape
     Hkv = k_cache.shape[2]
-    if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache/v_cache must share a shape with head dim d")
-    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
-        raise ValueError("seq_lens must be int32 [B]")
-    if block_table is not None:
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
-            raise ValueError("block_table must be int32 [B, max_blocks]")
-        if k_cache.shape[1] != BLOCK_TOKENS:
-            raise ValueError("a paged cache is [num_blocks, 16, Hkv, d]")
-    elif k_cache.shape[0] != B:
-        raise ValueError("a contiguous cache is [B, max_len, Hkv, d]")
     L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse")
+    _need_gpu(q, k_cache, v_cache, seq_lens, block_table, workspace, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, L, num_splits)
@@ -293,7 +338,6 @@ def attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=Non
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    _need_gpu(workspace, out, lse)
     st = lib.attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), mb,
                                nblocks, _ptr(seq_lens), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq,
                                Hkv, Nq, d, float(scale), int(bool(causal)), L, int(num_splits),
@@ -306,15 +350,17 @@ def attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=Non
 def kv_append(k_new, v_new, k_cache, v_cache, cache_lens, block_table=None, max_seq_len=None):
     """Write k_new/v_new [B,Nnew,Hkv,d] at positions cache_lens[b] + r (in place)."""
     lib = _load()
-    _need_gpu(k_new, v_new, k_cache, v_cache, cache_lens, block_table)
-    B, Nnew, Hkv, d = k_new.shape
+    B, Nnew, Hkv, d = _dims(k_new, 4, "k_new")
+    _dims(k_cache, 4, "k_cache")
     if v_new.shape != k_new.shape or k_cache.shape[2:] != (Hkv, d) or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch between new rows and cache")
     if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
         raise TypeError("new rows and cache must share one dtype")
     if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,):
         raise ValueError("cache_lens must be int32 [B]")
+    _check_table(block_table, k_cache, B)
     L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    _need_gpu(k_new, v_new, k_cache, v_cache, cache_lens, block_table)
     st = lib.kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                        mb, nblocks, _ptr(cache_lens), _dtype_code(k_new), B, Hkv, Nnew, d, L,
                        _stream(k_new.device))
@@ -336,8 +382,8 @@ def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_lens, 
     """Quantise k_new/v_new [B,Nnew,Hkv,d] (bf16) into an E4M3 cache at positions
     cache_lens[b] + r (in place); code = nearest(x / scale[h]), saturating at 448."""
     lib = _load()
-    _need_gpu(k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_lens, block_table)
-    B, Nnew, Hkv, d = k_new.shape
+    B, Nnew, Hkv, d = _dims(k_new, 4, "k_new")
+    _dims(k_cache, 4, "k_cache")
     if v_new.shape != k_new.shape or k_cache.shape[2:] != (Hkv, d) or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch between new rows and cache")
     if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
@@ -348,7 +394,9 @@ def kv_append_fp8(k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_lens, 
     _scales(v_scale, Hkv, k_cache.device)
     if cache_lens.dtype != torch.int32 or cache_lens.shape != (B,):
         raise ValueError("cache_lens must be int32 [B]")
+    _check_table(block_table, k_cache, B)
     L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    _need_gpu(k_new, v_new, k_cache, v_cache, k_scale, v_scale, cache_lens, block_table)
     st = lib.kv_append_fp8(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                            _ptr(v_scale), _ptr(block_table), mb, nblocks, _ptr(cache_lens), B, Hkv,
                            Nnew, d, L, _stream(k_new.device))
@@ -361,27 +409,15 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block
     """Decode against an E4M3 cache with per-head scales. q [B,Nq,Hq,d] bf16; caches
     uint8 [P,16,Hkv,d] (paged) or [B,L,Hkv,d]; -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
     lib = _load()
-    _need_gpu(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table)
+    _check_cache_args(q, k_cache, v_cache, seq_lens, block_table, fp8=True)
     B, Nq, Hq, d = q.shape
     Hkv = k_cache.shape[2]
-    if k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache/v_cache must share a shape with head dim d")
-    if q.dtype != torch.bfloat16:
-        raise TypeError("q is bf16")
-    _fp8_cache(k_cache)
-    _fp8_cache(v_cache)
-    _scales(k_scale, Hkv, q.device)
-    _scales(v_scale, Hkv, q.device)
-    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
-        raise ValueError("seq_lens must be int32 [B]")
-    if block_table is not None:
-        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
-            raise ValueError("block_table must be int32 [B, max_blocks]")
-        if k_cache.shape[1] != BLOCK_TOKENS:
-            raise ValueError("a paged cache is [num_blocks, 16, Hkv, d]")
-    elif k_cache.shape[0] != B:
-        raise ValueError("a contiguous cache is [B, max_len, Hkv, d]")
+    _scales(k_scale, Hkv, k_cache.device)
+    _scales(v_scale, Hkv, k_cache.device)
     L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse")
+    _need_gpu(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block_table, workspace, out, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, Nq, d, L, num_splits)
@@ -391,7 +427,6 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    _need_gpu(workspace, out, lse)
     st = lib.attn_decode_paged_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                    _ptr(v_scale), _ptr(block_table), mb, nblocks, _ptr(seq_lens),
                                    _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, d, float(scale),
@@ -405,13 +440,17 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, block
 def attn_gather_paged(cache, seq_lens, block_table=None, max_seq_len=None, out=None):
     """Gather each sequence's first seq_lens[b] rows into out [B, max_seq_len, Hkv, d]."""
     lib = _load()
-    _need_gpu(cache, seq_lens, block_table)
+    _dims(cache, 4, "cache")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1:
+        raise ValueError("seq_lens must be int32 [B]")
     B = seq_lens.shape[0]
     Hkv, d = cache.shape[2], cache.shape[3]
+    _check_table(block_table, cache, B)
     L, mb, nblocks = _cache_geometry(cache, block_table, max_seq_len)
+    _expect(out, (B, L, Hkv, d), cache.dtype, "out")
+    _need_gpu(cache, seq_lens, block_table, out)
     if out is None:
         out = torch.zeros((B, L, Hkv, d), dtype=cache.dtype, device=cache.device)
-    _need_gpu(out)
     st = lib.attn_gather_paged(_ptr(cache), _ptr(block_table), mb, nblocks, _ptr(seq_lens),
                                _ptr(out), _dtype_code(cache), B, Hkv, d, L, _stream(cache.device))
     _check(st, "attn_gather_paged")
