@@ -59,6 +59,13 @@ def _load():
     lib.attn_prefill.restype = I
     lib.attn_prefill_paged.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I, I, P]
     lib.attn_prefill_paged.restype = I
+    lib.attn_prefill_waves.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I, P]
+    lib.attn_prefill_waves.restype = I
+    lib.attn_prefill_paged_waves.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I,
+                                             I, I, P]
+    lib.attn_prefill_paged_waves.restype = I
+    lib.attn_prefill_workgroup_waves.argtypes = [I, I, I, I, I, I]
+    lib.attn_prefill_workgroup_waves.restype = I
     lib.attn_decode_paged_fp8.argtypes = [P, P, P, P, P, P, I, I, P, P, P, I, I, I, I, I, F, I, I,
                                           I, P, SZ, P]
     lib.attn_decode_paged_fp8.restype = I
@@ -155,8 +162,10 @@ def _expect(t, shape, dtype, name):
 
 
 def attn_prefill(q, k, v, scale=None, causal=False, q_offset=0, out=None, lse=None,
-                 want_lse=True):
-    """Prefill. q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d] -> o [B,Hq,Nq,d], lse [B,Hq,Nq] f32."""
+                 want_lse=True, waves=0):
+    """Prefill. q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d] -> o [B,Hq,Nq,d], lse [B,Hq,Nq] f32.
+    ``waves`` (tests): force the bf16 kernel's workgroup width, 4 or 8 (0 = the
+    library's choice, attn_prefill_workgroup_waves)."""
     lib = _load()
     B, Hq, Nq, d = _dims(q, 4, "q")
     _dims(k, 4, "k")
@@ -174,9 +183,12 @@ def attn_prefill(q, k, v, scale=None, causal=False, q_offset=0, out=None, lse=No
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    st = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq,
-                          Hkv, Nq, Nk, d, float(scale), int(bool(causal)), int(q_offset),
-                          _stream(q.device))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq, Hkv, Nq, Nk,
+            d, float(scale), int(bool(causal)), int(q_offset))
+    if waves:
+        st = lib.attn_prefill_waves(*args, int(waves), _stream(q.device))
+    else:
+        st = lib.attn_prefill(*args, _stream(q.device))
     _check(st, "attn_prefill")
     return out, lse
 
@@ -252,7 +264,7 @@ def _check_cache_args(q, k_cache, v_cache, seq_lens, block_table, fp8=False):
 
 
 def attn_prefill_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=None, causal=True,
-                       max_seq_len=None, out=None, lse=None, want_lse=True):
+                       max_seq_len=None, out=None, lse=None, want_lse=True, waves=0):
     """Chunked prefill against a cache. q [B,Nq,Hq,d]; caches [P,16,Hkv,d] (paged) or
     [B,L,Hkv,d] (contiguous); seq_lens [B] int32 (keys incl. the Nq new ones)
     -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
@@ -270,12 +282,22 @@ def attn_prefill_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=No
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    st = lib.attn_prefill_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), mb,
-                                nblocks, _ptr(seq_lens), _ptr(out), _ptr(lse), _dtype_code(q), B,
-                                Hq, Hkv, Nq, d, float(scale), int(bool(causal)), L,
-                                _stream(q.device))
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), mb, nblocks,
+            _ptr(seq_lens), _ptr(out), _ptr(lse), _dtype_code(q), B, Hq, Hkv, Nq, d, float(scale),
+            int(bool(causal)), L)
+    if waves:
+        st = lib.attn_prefill_paged_waves(*args, int(waves), _stream(q.device))
+    else:
+        st = lib.attn_prefill_paged(*args, _stream(q.device))
     _check(st, "attn_prefill_paged")
     return out, lse
+
+
+def attn_prefill_workgroup_waves(B, Hq, Hkv, Nq, causal, dtype=ATTN_BF16):
+    """Waves per workgroup (4 or 8) the bf16 prefill kernel picks for this shape."""
+    st = _load().attn_prefill_workgroup_waves(dtype, B, Hq, Hkv, Nq, int(bool(causal)))
+    _check(min(st, 0), "attn_prefill_workgroup_waves")
+    return st
 
 
 def attn_decode_num_splits(B, Hq, Hkv, Nq, d, max_seq_len, num_splits=0):
@@ -514,6 +536,7 @@ __all__ = [
     "attn_prefill_backward_workspace_bytes",
     "attn_prefill",
     "attn_prefill_paged",
+    "attn_prefill_workgroup_waves",
     "attn_decode_paged_fp8",
     "kv_append_fp8",
     "attn_decode_paged",

@@ -126,6 +126,20 @@ const char* attn_strerror(int status) {
 int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                  int q_offset, void* stream) {
+  return attn_prefill_waves(q, k, v, o, lse, dtype, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                            q_offset, 0, stream);
+}
+
+int attn_prefill_workgroup_waves(int dtype, int B, int Hq, int Hkv, int Nq, int causal) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Hq % Hkv != 0) return ATTN_EINVAL;
+  if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+  return attn::prefill_bf16_waves(B, Hq, Hkv, Nq, causal != 0, attn::device_compute_units());
+}
+
+int attn_prefill_waves(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                       int causal, int q_offset, int waves, void* stream) {
+  if (waves != 0 && (dtype != ATTN_BF16 || (waves != 4 && waves != 8))) return ATTN_EINVAL;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
@@ -141,6 +155,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* o, float* ls
       (reinterpret_cast<uintptr_t>(lse) & 3u))
     return ATTN_EINVAL;
   attn::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, q_offset};
+  a.waves = waves;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == ATTN_BF16 ? attn::launch_prefill_bf16(a, s)
                                       : attn::launch_prefill_f32(a, s));
@@ -199,6 +214,17 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* seq_lens, void* o, float* lse, int dtype, int B, int Hq,
                        int Hkv, int Nq, int d, float scale, int causal, int max_seq_len,
                        void* stream) {
+  return attn_prefill_paged_waves(q, k_cache, v_cache, block_table, max_blocks_per_seq,
+                                  num_blocks, seq_lens, o, lse, dtype, B, Hq, Hkv, Nq, d, scale,
+                                  causal, max_seq_len, 0, stream);
+}
+
+int attn_prefill_paged_waves(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                             const int32_t* seq_lens, void* o, float* lse, int dtype, int B,
+                             int Hq, int Hkv, int Nq, int d, float scale, int causal,
+                             int max_seq_len, int waves, void* stream) {
+  if (waves != 0 && waves != 4 && waves != 8) return ATTN_EINVAL;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || max_seq_len < 0) return ATTN_EINVAL;
   if (Hq % Hkv != 0) return ATTN_EINVAL;
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
@@ -222,6 +248,7 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
   a.num_blocks = block_table ? num_blocks : 0;
   a.max_len = max_seq_len;
   a.seq_lens = seq_lens;
+  a.waves = waves;
   return status_of(attn::launch_prefill_bf16(a, static_cast<hipStream_t>(stream)));
 }
 

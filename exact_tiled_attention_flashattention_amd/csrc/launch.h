@@ -27,7 +27,12 @@ struct PrefillArgs {
   const int32_t* block_table = nullptr;
   int max_blocks = 0, num_blocks = 0, max_len = 0;
   const int32_t* seq_lens = nullptr;
+  int waves = 0;  // bf16 workgroup width: 4 or 8, 0 = prefill_bf16_waves()
 };
+
+// Waves per workgroup the bf16 prefill kernel uses for a launch of this
+// shape when the caller does not force one (4 or 8).
+int prefill_bf16_waves(int B, int Hq, int Hkv, int Nq, int causal, int compute_units);
 
 struct DecodeArgs {
   const void* q;

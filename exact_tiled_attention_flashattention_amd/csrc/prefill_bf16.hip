@@ -552,6 +552,21 @@ hipError_t launch_d(const PrefillParams& pp, bool causal, bool cache, int nblock
 
 }  // namespace
 
+// 8-wave workgroups (the two waves on a SIMD step through the same tiles)
+// when they fill the chip: one per CU at least, and under a causal mask
+// (workgroups of unequal length) two per CU, so that long and short ones can
+// follow each other. Otherwise two 4-wave workgroups share each CU (a causal
+// prefill of 2048 rows: 49 against 58 us; a non-causal one of 1024 rows:
+// 27-30 against 36 us).
+int prefill_bf16_waves(int B, int Hq, int Hkv, int Nq, int causal, int compute_units) {
+  const int G = Hq / Hkv;
+  const int hw = (G % 4 == 0) ? 4 : ((G % 2 == 0) ? 2 : 1);
+  const long long per_row_block = (long long)B * Hkv * (G / hw);
+  const long long nq8 = (Nq + 32 * (8 / hw) - 1) / (32 * (8 / hw));
+  const long long need8 = (long long)compute_units * (causal ? 2 : 1);
+  return nq8 * per_row_block >= need8 ? 8 : 4;
+}
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   PrefillParams pp;
   pp.q = static_cast<const __bf16*>(a.q);
@@ -567,16 +582,10 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s) {
   pp.G = a.Hq / a.Hkv;
   pp.hw = (pp.G % 4 == 0) ? 4 : ((pp.G % 2 == 0) ? 2 : 1);
   pp.n_hgrp = pp.G / pp.hw;
-  // 8-wave workgroups (the two waves on a SIMD step through the same tiles)
-  // when they fill the chip: one per CU at least, and under a causal mask
-  // (workgroups of unequal length) two per CU, so that long and short ones
-  // can follow each other. Otherwise two 4-wave workgroups share each CU (a
-  // causal prefill of 2048 rows: 49 against 58 us; a non-causal one of 1024
-  // rows: 27-30 against 36 us).
-  const long long per_row_block = (long long)a.B * a.Hkv * pp.n_hgrp;
-  const long long nq8 = (a.Nq + 32 * (8 / pp.hw) - 1) / (32 * (8 / pp.hw));
-  const long long need8 = (long long)device_compute_units() * (a.causal ? 2 : 1);
-  const int W = nq8 * per_row_block >= need8 ? 8 : 4;
+  const int W = a.waves != 0 ? a.waves
+                             : prefill_bf16_waves(a.B, a.Hq, a.Hkv, a.Nq, a.causal,
+                                                  device_compute_units());
+  if (W != 4 && W != 8) return hipErrorInvalidValue;
   pp.pw = W / pp.hw;
   pp.n_qblk = (a.Nq + 32 * pp.pw - 1) / (32 * pp.pw);
   pp.c = a.scale * kLog2e;

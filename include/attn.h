@@ -259,6 +259,32 @@ int kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_c
                   int max_seq_len, void* stream);
 
 /*
+ * Workgroup width of the bf16 prefill kernel (attn_prefill and
+ * attn_prefill_paged) for a launch of this shape on the current device: 8
+ * waves when the launch gives at least one such workgroup per compute unit
+ * (two under a causal mask), else 4. Returns 4 or 8, or a negative
+ * attn_status (dtype other than ATTN_BF16: ATTN_EUNSUPPORTED). Host only.
+ */
+int attn_prefill_workgroup_waves(int dtype, int B, int Hq, int Hkv, int Nq, int causal);
+
+/*
+ * Test helpers: attn_prefill and attn_prefill_paged with the bf16 kernel's
+ * workgroup width forced (`waves` 4 or 8; 0 = the choice above), so that
+ * both kernel widths can be checked on any shape. Same arguments, results
+ * and errors as the calls they extend; a non-zero `waves` with dtype other
+ * than ATTN_BF16, or other than 4 or 8, is ATTN_EINVAL. The width changes
+ * only how rows are grouped into workgroups, never the result's definition.
+ */
+int attn_prefill_waves(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       float scale, int causal, int q_offset, int waves, void* stream);
+int attn_prefill_paged_waves(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, int max_blocks_per_seq,
+                             int num_blocks, const int32_t* seq_lens, void* o, float* lse,
+                             int dtype, int B, int Hq, int Hkv, int Nq, int d, float scale,
+                             int causal, int max_seq_len, int waves, void* stream);
+
+/*
  * Gather the first seq_lens[b] logical rows of every sequence out of a paged
  * (or, with block_table NULL, contiguous) cache into out [B, max_seq_len,
  * Hkv, d], using the same address computation as attn_decode_paged. Rows at

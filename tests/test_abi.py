@@ -296,3 +296,26 @@ def test_backward_workspace_size():
     assert f(-1, 1, 1, 1, 1, 64, 0, 0) == 0
     assert f(1, 4, 3, 1, 1, 64, 0, 0) == 0          # Hq % Hkv != 0
     assert f(1, 4, 2, 1, 1, 96, 0, 0) == 0          # head dim not built
+
+
+def test_prefill_width_override_rejects():
+    lib = eta.library()
+    args = [FAKE, FAKE, FAKE, FAKE, None, 1, 1, 4, 2, 8, 8, 128, ctypes.c_float(0.1), 1, 0]
+    assert lib.attn_prefill_waves(*args, 5, None) == eta.ATTN_EINVAL
+    args_f32 = list(args)
+    args_f32[5] = 0
+    assert lib.attn_prefill_waves(*args_f32, 8, None) == eta.ATTN_EINVAL
+    assert lib.attn_prefill_paged_waves(FAKE, FAKE, FAKE, FAKE, 4, 10, FAKE, FAKE, None, 1, 1, 4,
+                                        2, 8, 128, ctypes.c_float(0.1), 1, 64, 6,
+                                        None) == eta.ATTN_EINVAL
+
+
+def test_prefill_width_choice_on_the_host():
+    # with no device to query the library assumes 256 compute units
+    lib = eta.library()
+    assert lib.attn_prefill_workgroup_waves(1, 1, 32, 8, 4096, 1) == 8
+    assert lib.attn_prefill_workgroup_waves(1, 1, 32, 8, 2048, 1) == 4
+    assert lib.attn_prefill_workgroup_waves(1, 1, 32, 8, 2048, 0) == 8
+    assert lib.attn_prefill_workgroup_waves(1, 1, 8, 2, 300, 1) == 4
+    assert lib.attn_prefill_workgroup_waves(0, 1, 32, 8, 4096, 1) == eta.ATTN_EUNSUPPORTED
+    assert lib.attn_prefill_workgroup_waves(1, 1, 6, 4, 4096, 1) == eta.ATTN_EINVAL

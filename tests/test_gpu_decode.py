@@ -5,8 +5,8 @@ Covers contiguous and paged caches, Nq in {1, 2, 4, 5, 8, 64}, group sizes 1..16
 head dims 64/128, causal and not, explicit and default split counts, ragged
 lengths, rows that see no key, invalid table entries, NaN-poisoned unused
 cache rows, bitwise determinism and output guard bands; plus the split-KV
-decode workload (16 x 32k contiguous) and the paged 4-token workload on
-sampled (sequence, head) pairs at full size.
+decode workload (16 x 32k contiguous) and the paged 4-token workload,
+every output element, at full size in the launch the bench times.
 """
 
 import numpy as np
@@ -144,30 +144,39 @@ def test_decode_deterministic_and_guard_bands():
     assert guards_intact(buf_o) and guards_intact(buf_l)
 
 
-def test_splitkv_decode_32k_workload_sampled():
+def test_splitkv_decode_32k_workload_every_element():
+    """The 16 x 32k split-KV decode in the launch the bench times: every output
+    element and LSE (16 sequences x 32 heads) against the oracle."""
     dev = need_gpu()
     w = inputs.WORKLOADS["splitkv_decode_32k"]
     announce(f"workload splitkv_decode_32k: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} Nq=1 "
-             f"L={w['seq_len']} d={w['d']} contiguous, default splits")
+             f"L={w['seq_len']} d={w['d']} contiguous, default splits, every element")
     q, kc, vc, sl = inputs.workload_inputs("splitkv_decode_32k", dev)
     o, lse = eta.attn_decode_paged(q, kc, vc, sl, causal=True)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     G = w["Hq"] // w["Hkv"]
-    for b, hq in ((0, 0), (0, 31), (7, 13), (15, 4), (15, 30)):
-        g = hq // G
-        O, L = oracle.attention_rows(q[b, :, hq].cpu(), [w["seq_len"] - 1], kc[b, :, g].cpu(),
-                                     vc[b, :, g].cpu(), scale_of(w["d"]), True)
-        check(o[b, :, hq], O, lse[b, hq], L, "bf16", f"b={b} hq={hq}")
+    qc = q.cpu()
+    for b in range(w["B"]):
+        for g in range(w["Hkv"]):
+            K, V = kc[b, :, g].cpu(), vc[b, :, g].cpu()
+            for hq in range(g * G, (g + 1) * G):
+                O, L = oracle.attention_rows(qc[b, :, hq], [w["seq_len"] - 1], K, V,
+                                             scale_of(w["d"]), True)
+                check(o[b, :, hq], O, lse[b, hq], L, "bf16", f"b={b} hq={hq}")
 
 
-def test_paged_decode_q4_workload_sampled():
+def test_paged_decode_q4_workload_every_element():
+    """The paged 4-token decode in the launch the bench times (kv_append, then
+    decode): every output element and LSE of all 32 sequences x 32 heads x 4
+    rows, and the appended rows bit for bit."""
     dev = need_gpu()
     w = inputs.WORKLOADS["paged_decode_q4"]
     announce(f"workload paged_decode_q4: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} Nq=4 d={w['d']} "
-             "kv_append then decode")
+             "kv_append then decode, every element")
     inp = inputs.workload_inputs("paged_decode_q4", dev)
     k_new_cpu = inp["k_new"].cpu()
+    v_new_cpu = inp["v_new"].cpu()
     eta.kv_append(inp["k_new"], inp["v_new"], inp["k_pool"], inp["v_pool"], inp["cache_lens"],
                   block_table=inp["block_table"])
     o, lse = eta.attn_decode_paged(inp["q"], inp["k_pool"], inp["v_pool"], inp["seq_lens"],
@@ -176,9 +185,9 @@ def test_paged_decode_q4_workload_sampled():
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
     table = inp["block_table"].cpu()
     seq = inp["seq_lens"].cpu()
+    qc = inp["q"].cpu()
     G = w["Hq"] // w["Hkv"]
-    rng = np.random.default_rng(5)
-    for b in (0, 9, 21, 31):
+    for b in range(w["B"]):
         n = int(seq[b])
         nblk = (n + 15) // 16
         blocks = table[b, :nblk].long()
@@ -189,10 +198,10 @@ def test_paged_decode_q4_workload_sampled():
         V = oracle.gather_paged(vb, local, n)
         # the appended rows are exactly the new ones
         assert torch.equal(K[n - 4:].view(torch.int16), k_new_cpu[b].view(torch.int16))
-        for hq in rng.choice(w["Hq"], 3, replace=False):
-            hq = int(hq)
-            O, L = oracle.attention_rows(inp["q"][b, :, hq].cpu(), n - 4 + np.arange(4),
-                                         K[:, hq // G], V[:, hq // G], scale_of(w["d"]), True)
+        assert torch.equal(V[n - 4:].view(torch.int16), v_new_cpu[b].view(torch.int16))
+        for hq in range(w["Hq"]):
+            O, L = oracle.attention_rows(qc[b, :, hq], n - 4 + np.arange(4), K[:, hq // G],
+                                         V[:, hq // G], scale_of(w["d"]), True)
             check(o[b, :, hq], O, lse[b, hq], L, "bf16", f"b={b} hq={hq}")
 
 

@@ -159,7 +159,9 @@ def test_nan_codes_and_invalid_entries_do_not_leak():
     check(o, O, lse, L, "bf16", "fp8 with NaN codes and a hidden block")
 
 
-def test_fp8_workload_sampled():
+def test_fp8_workload_every_element():
+    """The paged 4-token decode over E4M3 codes at full size: every output
+    element and LSE of all 32 sequences x 32 heads, and every appended code."""
     dev = need_gpu()
     w = inputs.WORKLOADS["paged_decode_q4_fp8"]
     announce(f"workload paged_decode_q4_fp8: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} Nq=4 "
@@ -176,9 +178,10 @@ def test_fp8_workload_sampled():
     seq = inp["seq_lens"].cpu()
     ks, vs = _np(inp["k_scale"]), _np(inp["v_scale"])
     G = w["Hq"] // w["Hkv"]
-    rng = np.random.default_rng(7)
     knew = _np(inp["k_new"].cpu())
-    for b in (0, 11, 31):
+    qc = inp["q"].cpu()
+    vnew = _np(inp["v_new"].cpu())
+    for b in range(w["B"]):
         n = int(seq[b])
         nblk = (n + 15) // 16
         blocks = table[b, :nblk].long()
@@ -190,8 +193,9 @@ def test_fp8_workload_sampled():
         # the appended rows are the oracle's codes of the new rows
         codes = oracle.gather_paged(kb, local, n)[n - 4:]
         assert np.array_equal(codes, oracle.quantize(knew[b], ks))
-        for hq in rng.choice(w["Hq"], 3, replace=False):
-            hq = int(hq)
-            O, L = oracle.attention_rows(inp["q"][b, :, hq].cpu(), n - 4 + np.arange(4),
+        assert np.array_equal(oracle.gather_paged(vb, local, n)[n - 4:],
+                              oracle.quantize(vnew[b], vs))
+        for hq in range(w["Hq"]):
+            O, L = oracle.attention_rows(qc[b, :, hq], n - 4 + np.arange(4),
                                          K[:, hq // G], V[:, hq // G], scale_of(w["d"]), True)
             check(o[b, :, hq], O, lse[b, hq], L, "bf16", f"b={b} hq={hq}")

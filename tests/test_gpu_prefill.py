@@ -1,8 +1,9 @@
 """GPU parity of attn_prefill against the fp64 oracle (needs an MI355X).
 
 Small shapes are compared element by element over several tiles with ragged
-tails; the 4k and 32k causal GQA workloads are compared on sampled rows in
-the same launch configuration the bench times.
+tails; the 4k causal GQA workload is compared element by element, and the 32k
+one on every head and two rows of every 64-row query block, in the same
+launch configuration the bench times.
 """
 
 import numpy as np
@@ -76,37 +77,52 @@ def test_bf16_shapes(B, Hq, Hkv, Nq, Nk, d, causal, off):
     _run_full(dev, 12, B, Hq, Hkv, Nq, Nk, d, "bf16", causal, off)
 
 
-def _sampled(dev, name, heads, rows):
+def _workload_on_gpu(dev, name):
     w = inputs.WORKLOADS[name]
-    N, d = w["N"], w["d"]
-    announce(f"prefill workload {name}: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} N={N} d={d} "
-             f"causal, sampled heads {heads} x {len(rows)} rows")
-    q, k, v = inputs.prefill_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], N, N, d, "bf16", dev)
-    o, lse = eta.attn_prefill(q, k, v, scale=scale_of(d), causal=True)
+    q, k, v = inputs.prefill_inputs(w["seed"], w["B"], w["Hq"], w["Hkv"], w["N"], w["N"], w["d"],
+                                    "bf16", dev)
+    o, lse = eta.attn_prefill(q, k, v, scale=scale_of(w["d"]), causal=True)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    return w, q, k, v, o, lse
+
+
+def test_causal_gqa_prefill_4k_every_element():
+    """The 4k causal GQA workload in the launch the bench times: every output
+    element and every LSE of all 32 heads against the oracle."""
+    dev = need_gpu()
+    name = "causal_gqa_prefill_4k"
+    w, q, k, v, o, lse = _workload_on_gpu(dev, name)
+    announce(f"prefill workload {name}: B=1 Hq=32 Hkv=8 N=4096 d=128 causal, every element")
     G = w["Hq"] // w["Hkv"]
-    for hq in heads:
+    rows = np.arange(w["N"])
+    for hq in range(w["Hq"]):
         g = hq // G
-        qh = q[0, hq, rows].cpu()
-        O, L = oracle.attention_rows(qh, rows, k[0, g].cpu(), v[0, g].cpu(), scale_of(d), True)
-        check(o[0, hq, rows], O, lse[0, hq, rows], L, "bf16", f"head {hq}")
+        O, L = oracle.attention_rows(q[0, hq].cpu(), rows, k[0, g].cpu(), v[0, g].cpu(),
+                                     scale_of(w["d"]), True)
+        check(o[0, hq], O, lse[0, hq], L, "bf16", f"head {hq}")
 
 
-def test_causal_gqa_prefill_4k_sampled():
+def test_causal_gqa_prefill_32k_every_head_and_block():
+    """The 32k causal GQA workload in the launch the bench times: all 32 heads;
+    in each head the first row of every 64-row query block, one random row
+    inside every block, and the last row (1025 rows per head, 8.2 M outputs)."""
     dev = need_gpu()
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 127, 128, 2047, 2048, 4000, 4095],
-                                     rng.integers(0, 4096, 24)]))
-    _sampled(dev, "causal_gqa_prefill_4k", [0, 3, 4, 17, 31], rows)
-
-
-def test_causal_gqa_prefill_32k_sampled():
-    dev = need_gpu()
+    name = "causal_gqa_prefill_32k"
+    w, q, k, v, o, lse = _workload_on_gpu(dev, name)
+    N = w["N"]
+    announce(f"prefill workload {name}: B=1 Hq=32 Hkv=8 N={N} d=128 causal, every head, "
+             "two rows of every 64-row block")
+    G = w["Hq"] // w["Hkv"]
     rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 16383, 16384, 32703, 32767],
-                                     rng.integers(0, 32768, 16)]))
-    _sampled(dev, "causal_gqa_prefill_32k", [0, 9, 31], rows)
+    for hq in range(w["Hq"]):
+        g = hq // G
+        starts = np.arange(0, N, 64)
+        rows = np.unique(np.concatenate([starts, starts + rng.integers(1, 64, starts.size),
+                                         [N - 1]]))
+        K, V = k[0, g].cpu(), v[0, g].cpu()
+        O, L = oracle.attention_rows(q[0, hq, rows].cpu(), rows, K, V, scale_of(w["d"]), True)
+        check(o[0, hq, rows], O, lse[0, hq, rows], L, "bf16", f"head {hq} ({rows.size} rows)")
 
 
 def test_deterministic_and_guard_bands():
