@@ -34,6 +34,7 @@ ATTN_ENOSPACE = -5
 ATTN_F32 = 0
 ATTN_BF16 = 1
 BLOCK_TOKENS = 16
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_DECODE_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -74,6 +75,9 @@ def _load():
     lib.attn_decode_paged.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I, I, I,
                                       P, SZ, P]
     lib.attn_decode_paged.restype = I
+    lib.attn_decode_paged_noalloc.argtypes = [P, P, P, P, I, I, P, P, P, I, I, I, I, I, I, F, I,
+                                              I, I, P]
+    lib.attn_decode_paged_noalloc.restype = I
     lib.attn_decode_num_splits.argtypes = [I, I, I, I, I, I, I]
     lib.attn_decode_num_splits.restype = I
     lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
@@ -369,6 +373,35 @@ def attn_decode_paged(q, k_cache, v_cache, seq_lens, block_table=None, scale=Non
     return out, lse
 
 
+def attn_decode_paged_noalloc(q, k_cache, v_cache, seq_lens, block_table=None, scale=None,
+                              causal=True, max_seq_len=None, num_splits=0, out=None, lse=None,
+                              want_lse=True):
+    """attn_decode_paged whose partial results live in the library's own device
+    array (the C call allocates nothing; pass out/lse to allocate nothing here
+    either). Same arguments and results, no workspace; raises AttnError
+    (ATTN_EWORKSPACE) when the call needs more than NOALLOC_SCRATCH_BYTES."""
+    lib = _load()
+    _check_cache_args(q, k_cache, v_cache, seq_lens, block_table)
+    B, Nq, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    L, mb, nblocks = _cache_geometry(k_cache, block_table, max_seq_len)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, (B, Hq, Nq), torch.float32, "lse")
+    _need_gpu(q, k_cache, v_cache, seq_lens, block_table, out, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       mb, nblocks, _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                       _dtype_code(q), B, Hq, Hkv, Nq, d, float(scale),
+                                       int(bool(causal)), L, int(num_splits), _stream(q.device))
+    _check(st, "attn_decode_paged_noalloc")
+    return out, lse
+
+
 def kv_append(k_new, v_new, k_cache, v_cache, cache_lens, block_table=None, max_seq_len=None):
     """Write k_new/v_new [B,Nnew,Hkv,d] at positions cache_lens[b] + r (in place)."""
     lib = _load()
@@ -540,6 +573,7 @@ __all__ = [
     "attn_decode_paged_fp8",
     "kv_append_fp8",
     "attn_decode_paged",
+    "attn_decode_paged_noalloc",
     "attn_decode_num_splits",
     "attn_decode_workspace_bytes",
     "kv_append",

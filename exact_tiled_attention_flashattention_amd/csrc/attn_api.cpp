@@ -274,12 +274,12 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int d, int ma
 
 }  // extern "C"
 
-static int decode_impl(const void* q, const void* k_cache, const void* v_cache, int kv8,
-                       const float* k_scale, const float* v_scale, const int32_t* block_table,
-                       int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens, void* o,
-                       float* lse, int dtype, int B, int Hq, int Hkv, int Nq, int d, float scale,
-                       int causal, int max_seq_len, int num_splits, void* workspace,
-                       size_t workspace_bytes_given, void* stream) {
+int attn::decode_call(const void* q, const void* k_cache, const void* v_cache, int kv8,
+                      const float* k_scale, const float* v_scale, const int32_t* block_table,
+                      int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens, void* o,
+                      float* lse, int dtype, int B, int Hq, int Hkv, int Nq, int d, float scale,
+                      int causal, int max_seq_len, int num_splits, void* workspace,
+                      size_t workspace_bytes_given, void* stream, size_t* plan_bytes) {
   const int st = check_decode_shape(dtype, B, Hq, Hkv, Nq, d, max_seq_len, num_splits);
   if (st != ATTN_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f)) return ATTN_EINVAL;
@@ -297,6 +297,10 @@ static int decode_impl(const void* q, const void* k_cache, const void* v_cache, 
     return ATTN_EINVAL;
   const int workers = plan_workers(num_splits, Hq, Hkv, Nq, kv8 != 0);
   const WorkspaceLayout lay = workspace_layout(B, Hq, Hkv, Nq, d, workers);
+  if (plan_bytes != nullptr) {  // validation and sizing only
+    *plan_bytes = lay.total;
+    return ATTN_OK;
+  }
   if (workspace == nullptr || misaligned16(workspace) || workspace_bytes_given < lay.total)
     return ATTN_EWORKSPACE;
   attn::DecodeArgs a;
@@ -336,9 +340,10 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int Hkv, int Nq, int d, float scale, int causal, int max_seq_len,
                       int num_splits, void* workspace, size_t workspace_bytes_given,
                       void* stream) {
-  return decode_impl(q, k_cache, v_cache, 0, nullptr, nullptr, block_table, max_blocks_per_seq,
-                     num_blocks, seq_lens, o, lse, dtype, B, Hq, Hkv, Nq, d, scale, causal,
-                     max_seq_len, num_splits, workspace, workspace_bytes_given, stream);
+  return attn::decode_call(q, k_cache, v_cache, 0, nullptr, nullptr, block_table,
+                           max_blocks_per_seq, num_blocks, seq_lens, o, lse, dtype, B, Hq, Hkv,
+                           Nq, d, scale, causal, max_seq_len, num_splits, workspace,
+                           workspace_bytes_given, stream, nullptr);
 }
 
 int attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -348,9 +353,10 @@ int attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cach
                           int Nq, int d, float scale, int causal, int max_seq_len,
                           int num_splits, void* workspace, size_t workspace_bytes_given,
                           void* stream) {
-  return decode_impl(q, k_cache, v_cache, 1, k_scale, v_scale, block_table, max_blocks_per_seq,
-                     num_blocks, seq_lens, o, lse, ATTN_BF16, B, Hq, Hkv, Nq, d, scale, causal,
-                     max_seq_len, num_splits, workspace, workspace_bytes_given, stream);
+  return attn::decode_call(q, k_cache, v_cache, 1, k_scale, v_scale, block_table,
+                           max_blocks_per_seq, num_blocks, seq_lens, o, lse, ATTN_BF16, B, Hq,
+                           Hkv, Nq, d, scale, causal, max_seq_len, num_splits, workspace,
+                           workspace_bytes_given, stream, nullptr);
 }
 
 static int check_copy(const void* a, const void* b, const int32_t* block_table,

@@ -109,6 +109,18 @@ BackwardPlan plan_backward(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
 // be queried).
 int device_compute_units();
 
+// attn_decode_paged / attn_decode_paged_fp8 (kv8 != 0) after argument
+// validation. With plan_bytes != nullptr the call only validates its
+// arguments (the workspace aside) and stores the workspace bytes it needs,
+// launching nothing; a call with nothing to do (B or Nq zero) returns ATTN_OK
+// and leaves *plan_bytes untouched.
+int decode_call(const void* q, const void* k_cache, const void* v_cache, int kv8,
+                const float* k_scale, const float* v_scale, const int32_t* block_table,
+                int max_blocks_per_seq, int num_blocks, const int32_t* seq_lens, void* o,
+                float* lse, int dtype, int B, int Hq, int Hkv, int Nq, int d, float scale,
+                int causal, int max_seq_len, int num_splits, void* workspace,
+                size_t workspace_bytes, void* stream, size_t* plan_bytes);
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t s);

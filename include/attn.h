@@ -34,7 +34,9 @@
  *     scaled-score units: LSE_i = ln Σ_{visible j} exp(scale · q_i·k_j).
  *     A row that sees no key gets O = 0 and LSE = -inf.
  *   - Kernels use no atomics: results are bitwise reproducible run to run.
- *   - The library is stateless and re-entrant.
+ *   - The library is stateless and re-entrant, with one exception:
+ *     attn_decode_paged_noalloc keeps its scratch in a device array of its
+ *     own (one per GPU) and the array's address per device.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -179,6 +181,31 @@ int attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cach
                           int B, int Hq, int Hkv, int Nq, int d,
                           float scale, int causal, int max_seq_len, int num_splits,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The partial results live in a
+ * library-owned device array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES bytes, one
+ * per GPU, held from the first call on that GPU until the process ends; the
+ * call allocates and frees nothing. Arguments, layouts, results and errors as
+ * attn_decode_paged (same kernels, same bits), except: a call whose
+ * attn_decode_workspace_bytes() exceeds the array returns ATTN_EWORKSPACE
+ * and enqueues nothing. At d = 128, Hkv = 8 and the default 1024 workers of
+ * a 256-CU device the 32 MiB hold up to 1903 sequences with 4 query rows per
+ * K/V head, 379 with 16, 190 with 32 and 95 with 64.
+ * Every call on one GPU shares that GPU's array, and everything in it is
+ * written before it is read within a call: calls that may overlap on one GPU
+ * (other streams, other host threads) race and must be ordered by the
+ * caller.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, int max_blocks_per_seq, int num_blocks,
+                              const int32_t* seq_lens, void* o, float* lse,
+                              int dtype, int B, int Hq, int Hkv, int Nq, int d,
+                              float scale, int causal, int max_seq_len, int num_splits,
+                              void* stream);
 
 /* Worker count attn_decode_paged uses for these arguments (num_splits = 0:
  * the default for the current device), or a negative attn_status. */

@@ -319,3 +319,21 @@ def test_prefill_width_choice_on_the_host():
     assert lib.attn_prefill_workgroup_waves(1, 1, 8, 2, 300, 1) == 4
     assert lib.attn_prefill_workgroup_waves(0, 1, 32, 8, 4096, 1) == eta.ATTN_EUNSUPPORTED
     assert lib.attn_prefill_workgroup_waves(1, 1, 6, 4, 4096, 1) == eta.ATTN_EINVAL
+
+
+def test_noalloc_decode_rejects_before_any_device_call():
+    lib = eta.library()
+    f = ctypes.c_float(0.1)
+    # a call that would need more than the library's static array
+    big = lib.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, 8, 100000, FAKE, FAKE, None, 1,
+                                        400, 32, 8, 4, 128, f, 1, 4096, 0, None)
+    assert big == eta.ATTN_EWORKSPACE
+    assert eta.attn_decode_workspace_bytes(400, 32, 8, 4, 128, 4096) > eta.NOALLOC_SCRATCH_BYTES
+    # the usual argument checks come first
+    assert lib.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, 8, 100, FAKE, FAKE, None, 1, 4,
+                                         6, 4, 1, 128, f, 1, 128, 0, None) == eta.ATTN_EINVAL
+    assert lib.attn_decode_paged_noalloc(FAKE, FAKE, FAKE, FAKE, 8, 100, FAKE, FAKE, None, 0, 4,
+                                         8, 2, 1, 128, f, 1, 128, 0, None) == eta.ATTN_EUNSUPPORTED
+    # nothing to do: no device is touched
+    assert lib.attn_decode_paged_noalloc(None, None, None, None, 0, 0, None, None, None, 1, 0, 8,
+                                         2, 1, 128, f, 1, 128, 0, None) == eta.ATTN_OK
