@@ -163,9 +163,20 @@ class StageTimer:
         ev1.record(self.stream)
         self.pairs[name].append((ev0, ev1))
 
+    def times_ms(self, name):
+        return [a.elapsed_time(b) for a, b in self.pairs[name]]
+
     def mean_ms(self, name):
-        ps = self.pairs[name]
-        return sum(a.elapsed_time(b) for a, b in ps) / len(ps)
+        ts = self.times_ms(name)
+        return sum(ts) / len(ts)
+
+    def stats(self, name):
+        """mean, median and min of the event-timed durations, in ms"""
+        ts = sorted(self.times_ms(name))
+        n = len(ts)
+        med = ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2])
+        return {"ms": round(sum(ts) / n, 5), "ms_median": round(med, 5), "ms_min": round(ts[0], 5),
+                "launches": n}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters_all_workloads.md")
@@ -197,53 +208,157 @@ def counter_traffic(stage, kernel, sources):
     return None
 
 
-def cpu_baseline(q, k, v, min_seconds=10.0, max_heads=128):
-    """Time the fp64 oracle on whole heads (all 4096 rows) of the 4k causal prefill,
-    cycling over the 32 heads until about `min_seconds` of CPU work is done."""
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the visible cores
+        return os.cpu_count()
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _single_thread(fn):
+    """Run fn() with BLAS limited to one thread; None when that cannot be arranged."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+
+def cpu_baselines(torch, inputs, dev, seconds=5.0):
+    """The fp64 oracle, timed on the host's cores on bounded samples of every
+    workload (about 20-30 s of CPU work in all), each rate scaled by the same
+    convention as the GPU figure (visible pairs x 4d FLOP; each visible K/V row
+    once for decode). Returns the headline workload's figure with the others
+    under "per_workload"."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
+    threads = _blas_threads()
+    out = {}
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: report the visible cores
-        threads = os.cpu_count()
-    qc = q.cpu()
-    kc = k.cpu()
-    vc = v.cpu()
-    d = q.shape[-1]
-    G = q.shape[1] // k.shape[1]
-    Hq = q.shape[1]
-    done = 0
-    t0 = time.perf_counter()
-    while done < max_heads and (done < 1 or time.perf_counter() - t0 < min_seconds):
+    # 4k causal GQA prefill: whole heads (all 4096 rows), cycling over the 32
+    q, k, v = (t.cpu() for t in inputs.workload_inputs("causal_gqa_prefill_4k", dev))
+    N, d, G, Hq = q.shape[2], q.shape[3], q.shape[1] // k.shape[1], q.shape[1]
+    rows = np.arange(N)
+    done, t0 = 0, time.perf_counter()
+    while done < 1 or (time.perf_counter() - t0 < seconds and done < 4 * Hq):
         hq = done % Hq
-        oracle.attention_rows(qc[0, hq], np.arange(q.shape[2]), kc[0, hq // G], vc[0, hq // G],
-                              1.0 / math.sqrt(d), True)
+        oracle.attention_rows(q[0, hq], rows, k[0, hq // G], v[0, hq // G], 1 / math.sqrt(d), True)
         done += 1
     dt = time.perf_counter() - t0
-    flops = prefill_flops(1, done, q.shape[2], d)
-    out = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-           "kind": "oracle",
-           "sample": f"{done} head passes (heads taken in order, cycling over the {Hq}), all "
-                     f"{q.shape[2]} rows each, of the causal GQA 4k prefill (fp64 numpy, "
-                     f"{dt:.1f} s)"}
-    # the same oracle on one core: one head pass with BLAS limited to one thread
-    try:
-        from threadpoolctl import threadpool_limits
+    rate = prefill_flops(1, done, N, d) / dt / 1e12
+    one = _single_thread(lambda: oracle.attention_rows(q[0, 0], rows, k[0, 0], v[0, 0],
+                                                       1 / math.sqrt(d), True))
+    out["causal_gqa_prefill_4k"] = {
+        "value": round(rate, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"{done} whole heads (all {N} rows; heads in order, cycling over the {Hq}), "
+                  f"{dt:.1f} s",
+        "single_core_value": (round(prefill_flops(1, 1, N, d) / one / 1e12, 6) if one else None),
+        "whole_workload_s_estimate": round(prefill_flops(1, Hq, N, d) / (rate * 1e12), 2)}
+    del q, k, v
 
-        with threadpool_limits(limits=1):
-            t1 = time.perf_counter()
-            oracle.attention_rows(qc[0, 0], np.arange(q.shape[2]), kc[0, 0], vc[0, 0],
-                                  1.0 / math.sqrt(d), True)
-            d1 = time.perf_counter() - t1
-        out["single_core_value"] = round(prefill_flops(1, 1, q.shape[2], d) / d1 / 1e12, 6)
-        out["single_core_sample"] = f"1 head pass of the same workload on 1 thread ({d1:.1f} s)"
-    except Exception:  # threadpoolctl missing: no single-core figure
-        pass
-    return out
+    # 32k causal GQA prefill: every 16th row of one head (2048 rows spread over
+    # the whole causal triangle, so their visible pairs average those of the
+    # head), extrapolated to the workload
+    q, k, v = inputs.workload_inputs("causal_gqa_prefill_32k", dev)
+    N3 = q.shape[2]
+    rows3 = np.arange(0, N3, 16)
+    qh, kh, vh = q[0, 0, rows3].cpu(), k[0, 0].cpu(), v[0, 0].cpu()
+    del q, k, v
+    t0 = time.perf_counter()
+    oracle.attention_rows(qh, rows3, kh, vh, 1 / math.sqrt(d), True)
+    dt = time.perf_counter() - t0
+    fl = 4.0 * d * float((rows3 + 1).sum())
+    rate = fl / dt / 1e12
+    out["causal_gqa_prefill_32k"] = {
+        "value": round(rate, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": f"rows 0, 16, 32, ... ({rows3.size} rows) of head 0 against all {N3} keys, "
+                  f"{dt:.1f} s; the whole workload is extrapolated at that rate",
+        "whole_workload_s_estimate": round(prefill_flops(1, 32, N3, d) / (rate * 1e12), 1),
+        "extrapolated": True}
+    del qh, kh, vh
+
+    # 16 x 32k split-KV decode: whole sequences (every head), until the budget is spent
+    w4 = inputs.WORKLOADS["splitkv_decode_32k"]
+    q, kc, vc, sl = inputs.workload_inputs("splitkv_decode_32k", dev)
+    qc, slc = q.cpu(), sl.cpu()
+    per_seq = 2 * 2 * w4["Hkv"] * w4["d"] * w4["seq_len"]
+    done, t0, t_copy = 0, time.perf_counter(), 0.0
+    while done < 1 or (time.perf_counter() - t0 - t_copy < seconds and done < w4["B"]):
+        b = done
+        tc = time.perf_counter()
+        kb, vb = kc[b:b + 1].cpu(), vc[b:b + 1].cpu()  # the device-to-host copy is not timed
+        t_copy += time.perf_counter() - tc
+        oracle.decode_attention(qc[b:b + 1], kb, vb, slc[b:b + 1], 1 / math.sqrt(w4["d"]), True)
+        done += 1
+    dt = time.perf_counter() - t0 - t_copy
+    del q, kc, vc
+    out["splitkv_decode_32k"] = {
+        "value": round(done * per_seq / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {w4['B']} sequences, every head ({dt:.1f} s of oracle time)",
+        "whole_workload_s_estimate": round(w4["B"] * dt / done, 2)}
+
+    # paged 4-token decode (bf16 cache): whole sequences through the oracle's gather
+    w5 = inputs.WORKLOADS["paged_decode_q4"]
+    p = inputs.workload_inputs("paged_decode_q4", dev)
+    kp, vp = p["k_pool"].cpu(), p["v_pool"].cpu()
+    qc, tab, seq = p["q"].cpu(), p["block_table"].cpu(), p["seq_lens"].cpu()
+    del p
+    done, t0, nbytes = 0, time.perf_counter(), 0
+    while done < 1 or (time.perf_counter() - t0 < seconds and done < w5["B"]):
+        b = done
+        oracle.decode_attention(qc[b:b + 1], kp, vp, seq[b:b + 1], 1 / math.sqrt(w5["d"]), True,
+                                block_table=tab[b:b + 1])
+        nbytes += 2 * 2 * w5["Hkv"] * w5["d"] * int(seq[b])
+        done += 1
+    dt = time.perf_counter() - t0
+    allb = 2 * 2 * w5["Hkv"] * w5["d"] * int(seq.sum())
+    out["paged_decode_q4"] = {
+        "value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"{done} of {w5['B']} sequences, every head ({dt:.1f} s)",
+        "whole_workload_s_estimate": round(allb / (nbytes / dt), 2)}
+    del kp, vp
+
+    # single-head fp32 256 x 64: the whole workload, all cores and one core
+    q, k, v = (t.cpu() for t in inputs.workload_inputs("single_head_f32", dev))
+    n1 = q.shape[2]
+    rows1 = np.arange(n1)
+    reps, t0 = 0, time.perf_counter()
+    while reps < 20 or time.perf_counter() - t0 < 0.5:
+        oracle.attention_rows(q[0, 0], rows1, k[0, 0], v[0, 0], 0.125, False)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    one = _single_thread(lambda: [oracle.attention_rows(q[0, 0], rows1, k[0, 0], v[0, 0], 0.125,
+                                                        False) for _ in range(20)])
+    out["single_head_f32"] = {
+        "us": round(dt * 1e6, 1), "cores": threads, "kind": "oracle",
+        "sample": f"the whole workload, {reps} repetitions",
+        "single_core_us": round(one / 20 * 1e6, 1) if one else None}
+
+    head = dict(out["causal_gqa_prefill_4k"])
+    head["host"] = cpu_model()
+    head["host_cpus"] = os.cpu_count()
+    head["per_workload"] = {k2: v2 for k2, v2 in out.items() if k2 != "causal_gqa_prefill_4k"}
+    return head
 
 
 def main():
@@ -332,7 +447,7 @@ def main():
     ms2 = timer.mean_ms("prefill_4k")
     tflops2 = flops2 / (ms2 * 1e-3) / 1e12
     result_workloads = {
-        "causal_gqa_prefill_4k": {"ms": round(ms2, 5), "TFLOP/s": round(tflops2, 2),
+        "causal_gqa_prefill_4k": {**timer.stats("prefill_4k"), "TFLOP/s": round(tflops2, 2),
                                   "frac_of_peak": round(tflops2 / PEAK_BF16_TFLOPS, 4),
                                   "flops": flops2},
     }
@@ -342,13 +457,13 @@ def main():
     ms5 = timer.mean_ms("paged_decode_q4")
     msa = timer.mean_ms("kv_append_q4")
     result_workloads["splitkv_decode_32k"] = {
-        "ms": round(ms4, 5), "GB/s": round(bytes4 / (ms4 * 1e-3) / 1e9, 1),
+        **timer.stats("splitkv_decode_32k"), "GB/s": round(bytes4 / (ms4 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kv_bytes": bytes4,
         "traffic_partial_kernel": counter_traffic("splitkv_decode_32k", "decode_partial_kernel<128,false>",
                                                   ["common.h", "decode.hip"])}
     result_workloads["paged_decode_q4"] = {
-        "ms": round(ms5, 5), "GB/s": round(bytes5 / (ms5 * 1e-3) / 1e9, 1),
+        **timer.stats("paged_decode_q4"), "GB/s": round(bytes5 / (ms5 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes5 / (ms5 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kv_bytes": bytes5, "kv_append_ms": round(msa, 5),
         "traffic_partial_kernel": counter_traffic("paged_decode_q4", "decode_partial_kernel<128,false>",
@@ -369,7 +484,7 @@ def main():
     ms3 = t3.mean_ms("p")
     flops3 = prefill_flops(1, 32, 32768, 128)
     result_workloads["causal_gqa_prefill_32k"] = {
-        "ms": round(ms3, 4), "TFLOP/s": round(flops3 / (ms3 * 1e-3) / 1e12, 2),
+        **t3.stats("p"), "TFLOP/s": round(flops3 / (ms3 * 1e-3) / 1e12, 2),
         "frac_of_peak": round(flops3 / (ms3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops": flops3}
     del q3, k3, v3, o3, l3
@@ -395,7 +510,7 @@ def main():
     ms6 = t6.mean_ms("p")
     flops6 = chunk_flops([int(x) for x in p6["seq_lens"].cpu()], w6["Nq"], w6["Hq"], w6["d"])
     result_workloads["chunked_prefill_paged"] = {
-        "ms": round(ms6, 5), "TFLOP/s": round(flops6 / (ms6 * 1e-3) / 1e12, 2),
+        **t6.stats("p"), "TFLOP/s": round(flops6 / (ms6 * 1e-3) / 1e12, 2),
         "frac_of_peak": round(flops6 / (ms6 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops": flops6}
     del p6, o6, l6
@@ -422,7 +537,7 @@ def main():
     ms8 = t8.mean_ms("p")
     flops8 = 2.5 * prefill_flops(w8["B"], w8["Hq"], w8["N"], w8["d"])
     result_workloads["causal_gqa_backward_4k"] = {
-        "ms": round(ms8, 5), "TFLOP/s": round(flops8 / (ms8 * 1e-3) / 1e12, 2),
+        **t8.stats("p"), "TFLOP/s": round(flops8 / (ms8 * 1e-3) / 1e12, 2),
         "frac_of_peak": round(flops8 / (ms8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flops": flops8,
         "flop_convention": "five products per visible pair (QK^T, dO V^T, P^T dO, dS K, dS^T Q),"
@@ -459,7 +574,7 @@ def main():
     ms7 = t7.mean_ms("d")
     bytes7 = 2 * 1 * w7["Hkv"] * w7["d"] * sum(seq7)
     result_workloads["paged_decode_q4_fp8"] = {
-        "ms": round(ms7, 5), "GB/s": round(bytes7 / (ms7 * 1e-3) / 1e9, 1),
+        **t7.stats("d"), "GB/s": round(bytes7 / (ms7 * 1e-3) / 1e9, 1),
         "frac_of_peak": round(bytes7 / (ms7 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
         "kv_bytes": bytes7, "kv_append_ms": round(t7.mean_ms("a"), 5),
         "speedup_vs_bf16_cache": round(ms5 / ms7, 3),
@@ -475,7 +590,11 @@ def main():
     for _ in range(50):
         t1.run("p", lambda: eta.attn_prefill(q1, k1, v1, causal=False))
     torch.cuda.synchronize()
-    result_workloads["single_head_f32"] = {"us": round(t1.mean_ms("p") * 1e3, 2)}
+    st1 = t1.stats("p")
+    result_workloads["single_head_f32"] = {"us": round(st1["ms"] * 1e3, 2),
+                                           "us_median": round(st1["ms_median"] * 1e3, 2),
+                                           "us_min": round(st1["ms_min"] * 1e3, 2),
+                                           "launches": st1["launches"]}
 
     traffic = counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true,false,8>",
                               ["common.h", "prefill_bf16.hip"])
@@ -484,6 +603,38 @@ def main():
                 "traffic": traffic, "traffic_unit": "bytes per launch (HBM read + write)",
                 "kernel": "prefill_bf16_kernel<128, true, false, 8>",
                 "per_launch": f"{flops2:.6g} FLOP (visible pairs x 4d) per launch"}
+
+    # one roofline object per named workload (the decode ones against HBM)
+    def _mfma(name, kernel, stage):
+        r = result_workloads[name]
+        return {"bound": "mfma", "achieved": r["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": r["frac_of_peak"], "kernel": kernel,
+                "traffic": counter_traffic(stage, kernel.replace(" ", ""),
+                                           ["common.h", "prefill_bf16.hip"]),
+                "per_launch": f"{r['flops']:.6g} FLOP (visible pairs x 4d)"}
+
+    def _hbm(name, stage, kernels):
+        r = result_workloads[name]
+        tr = [counter_traffic(stage, k.replace(" ", ""), ["common.h", "decode.hip"])
+              for k in kernels]
+        return {"bound": "hbm", "achieved": r["GB/s"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": r["frac_of_peak"], "kernel": " + ".join(kernels),
+                "traffic": None if None in tr else sum(tr),
+                "per_launch": f"{r['kv_bytes']} B of K/V (each visible row once)"}
+
+    rooflines = {
+        "causal_gqa_prefill_4k": roofline,
+        "causal_gqa_prefill_32k": _mfma("causal_gqa_prefill_32k",
+                                        "prefill_bf16_kernel<128, true, false, 8>", "prefill_32k"),
+        "splitkv_decode_32k": _hbm("splitkv_decode_32k", "splitkv_decode_32k",
+                                   ["decode_partial_kernel<128, false>",
+                                    "decode_combine_kernel<128>"]),
+        "paged_decode_q4": _hbm("paged_decode_q4", "paged_decode_q4",
+                                ["decode_partial_kernel<128, false>",
+                                 "decode_combine_kernel<128>"]),
+        "single_head_f32": {"bound": "latency", "us": result_workloads["single_head_f32"]["us"],
+                            "per_launch": "16.8 MFLOP (256 x 256 x 64 x 4), one head"},
+    }
 
     if not args.no_chat_sim:
         from exact_tiled_attention_flashattention_amd import chat_sim
@@ -504,9 +655,9 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(q2, k2, v2)
-        cpu["host"] = platform.processor() or platform.machine()
-        cpu["host_cpus"] = os.cpu_count()
+        del q2, k2, v2, p5, ws4, ws5
+        torch.cuda.empty_cache()
+        cpu = cpu_baselines(torch, inputs, dev)
 
     line = {
         "metric": METRIC,
@@ -523,8 +674,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "causal_gqa_prefill_4k", "B": 1, "Hq": 32, "Hkv": 8, "N": 4096,
                    "d": 128, "causal": True,
-                   "step": [n for n, _ in stages]},
+                   "step": [n for n, _ in stages],
+                   "timing": "HIP events on the library's stream; ms = mean, with median and "
+                             "min, over the timed launches"},
         "roofline": roofline,
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
         "workloads": result_workloads,
     }
