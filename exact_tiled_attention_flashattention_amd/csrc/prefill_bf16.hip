@@ -85,6 +85,16 @@ __device__ __forceinline__ int lds_off(int row, int elem) {  // byte offset of e
   return row * (D * 2) + ((((elem >> 3) ^ swz<D>(row))) << 4) + ((elem & 7) << 1);
 }
 
+// V tiles live in LDS in column blocks: the 64 rows of elements [32c, 32c + 32)
+// form a 4 KiB block, 64 bytes per row. The transposing reads of PV (4
+// consecutive rows x 64 bytes per 32 lanes) then touch 256 contiguous bytes,
+// conflict-free without a swizzle, and every read of a wave differs from the
+// others by a constant: one address register serves them all.
+constexpr int kVBlockBytes = kBN * 64;
+__device__ __forceinline__ int v_lds_off(int row, int elem) {
+  return (elem >> 5) * kVBlockBytes + row * 64 + ((elem & 31) << 1);
+}
+
 // kWaves waves per workgroup: 8 (one workgroup fills a CU) or 4 (two share
 // one) -- see launch_prefill_bf16
 template <int D, bool CAUSAL, bool CACHE, int kWaves>
@@ -224,6 +234,21 @@ void prefill_bf16_kernel(PrefillParams p) {
                                                soff + i * RPI * row_bytes, 0, 0);
   };
 
+  // V into the column-block layout: instruction j of a tile (1 KiB) holds
+  // rows 16*(j%4) + lane/4 of column block j/4, 16 bytes (lane%4) each.
+  auto load_v_rows = [&](__amdgpu_buffer_rsrc_t rs, int soff, int row_bytes, char* dst)
+      __attribute__((always_inline)) {
+    int lb = (lane >> 2) * row_bytes + 16 * (lane & 3);
+    asm volatile("" : "+v"(lb));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int j = wave * NI + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(dst + j * 1024), 16, lb,
+                                               soff + 16 * (j & 3) * row_bytes + 64 * (j >> 2),
+                                               0, 0);
+    }
+  };
+
   // [B, Hkv, Nk, D] slabs: one resource per K/V head (range Nk rows); the
   // tile's rows are contiguous, wave w's share starts at row (64/kWaves)*w.
   const long long kv_base = CACHE ? 0 : ((long long)b * p.Hkv + kvh) * (long long)p.Nk * D;
@@ -280,19 +305,35 @@ void prefill_bf16_kernel(PrefillParams p) {
     }
     if (4 * t + 7 >= wbase + 64) fetch(max(0, 4 * t - 4));
   };
-  auto load_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
-    // the waves split the tile's four 16-token blocks evenly: wave w loads
-    // rows [16/WB*(w%WB), +16/WB) of block 4t + w/WB, WB = waves per block
-    constexpr int WB = kWaves / 4;
-    const int jb = 4 * t + wave / WB;
+  auto block_rsrc = [&](const __bf16* pool, int jb) __attribute__((always_inline)) {
     const int i = jb - wbase;
     const long long off = ((long long)__builtin_amdgcn_readlane(woff_hi, i) << 32) |
                           (unsigned)__builtin_amdgcn_readlane(woff_lo, i);
     const int valid = min(kBlockTokens, nk - kBlockTokens * jb);
     const bool ok = ((wst >> i) & 1ull) != 0 && valid > 0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+    return __builtin_amdgcn_make_buffer_rsrc(
         (void*)(pool + (ok ? off : 0)), 0, ok ? (valid - 1) * rowb + D * 2 : 0, kBufferFlags);
-    load_rows(rs, (wave % WB) * (kBlockTokens / WB) * rowb, rowb, dst);
+  };
+  // the waves split the tile's four 16-token blocks evenly, WB = waves per block
+  constexpr int WB = kWaves / 4;
+  auto load_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
+    // K: wave w loads rows [16/WB*(w%WB), +16/WB) of block 4t + w/WB
+    load_rows(block_rsrc(pool, 4 * t + wave / WB), (wave % WB) * (kBlockTokens / WB) * rowb,
+              rowb, dst);
+  };
+  auto load_v_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
+    // V: wave w loads column blocks [NI*(w%WB), +NI) of block q = w/WB, the
+    // block's 16 rows of each (LDS bytes 1024*q of the column block)
+    const int q = wave / WB;
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(pool, 4 * t + q);
+    int lb = (lane >> 2) * rowb + 16 * (lane & 3);
+    asm volatile("" : "+v"(lb));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int db = (wave % WB) * NI + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (ATTN_LDS void*)(dst + db * kVBlockBytes + q * 1024), 16, lb, 64 * db, 0, 0);
+    }
   };
   // bit q: block 4t + q of tile t has storage (blocks past the sequence count
   // as present; their keys are masked by position)
@@ -312,9 +353,9 @@ void prefill_bf16_kernel(PrefillParams p) {
   };
   auto issue_v = [&](int t, char* dst) __attribute__((always_inline)) {
     if constexpr (CACHE)
-      load_block(p.v, t, dst);
+      load_v_block(p.v, t, dst);
     else
-      load_rows(vrs, t * kBN * D * 2 + wave * NI * 1024, D * 2, dst);
+      load_v_rows(vrs, t * kBN * D * 2, D * 2, dst);
   };
   // block bits of tiles it, it+1, it+2 in bits [3:0], [7:4], [11:8]
   unsigned okq = 0xFFFu;
@@ -449,9 +490,9 @@ void prefill_bf16_kernel(PrefillParams p) {
         for (int db = 0; db < NDB; ++db) {
           const int col = 32 * db + tr_col;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (ATTN_LDS i16x4_t*)(vc + lds_off<D>(r0, col)));
+              (ATTN_LDS i16x4_t*)(vc + v_lds_off(r0, col)));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (ATTN_LDS i16x4_t*)(vc + lds_off<D>(r0 + 8, col)));
+              (ATTN_LDS i16x4_t*)(vc + v_lds_off(r0 + 8, col)));
           const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
           const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};

@@ -107,3 +107,26 @@ def test_library_width_choice():
     # the small test shapes run 4-wave workgroups
     for B, Hq, Hkv, Nq, _, _ in SLABS:
         assert eta.attn_prefill_workgroup_waves(B, Hq, Hkv, Nq, True) == 4
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_cache_widths_ignore_nan_in_unused_rows(d, waves):
+    """Both widths read a partly filled 16-token block through a range that
+    ends at its last valid row: NaN in the unused slots and spare blocks must
+    not reach the output."""
+    dev = need_gpu()
+    announce(f"paged prefill waves={waves} d={d} with NaN-poisoned unused rows, B=3 Hq=8 Hkv=2 "
+             f"Nq=50")
+    inp = inputs.paged_inputs(90 + d, 3, 8, 2, 50, d, 30, 200, spare_blocks=16)
+    kp = oracle.kv_append_ref(inp["k_pool"], inp["k_new"], inp["block_table"], inp["cache_lens"])
+    vp = oracle.kv_append_ref(inp["v_pool"], inp["v_new"], inp["block_table"], inp["cache_lens"])
+    inp["k_pool"], inp["v_pool"] = kp, vp
+    assert inputs.poison_unused(inp) > 0
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    o, lse = eta.attn_prefill_paged(g["q"], g["k_pool"], g["v_pool"], g["seq_lens"],
+                                    block_table=g["block_table"], causal=True, waves=waves)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_attention(inp["q"], kp, vp, inp["seq_lens"], scale_of(d), True,
+                                   block_table=inp["block_table"])
+    check(o, O, lse, L, "bf16", f"poisoned pool, waves={waves}")
