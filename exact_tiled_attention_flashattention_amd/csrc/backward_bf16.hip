@@ -34,6 +34,8 @@
 // XOR-swizzled LDS layout in which both the row reads (MFMA A operand) and
 // the transposing reads are conflict-free, double-buffered (triple-buffered
 // in the dK/dV kernel) with one barrier per tile.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -71,58 +73,90 @@ struct BwdParams {
   int causal;
 };
 
-// Tile rows live in LDS unpadded (D*2 bytes per row) with the 16-byte chunks
-// of row r permuted by chunk ^ swz(r): 16 consecutive rows read at one chunk
-// and the transposing reads (4 rows x 4 chunks per 32 lanes) both hit
-// distinct banks.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (D == 128)
-    return ((row & 3) << 2) | ((row >> 2) & 3);
-  else
-    return (row >> 1) & 7;
-}
+// Tiles (64 rows of D bf16) live in LDS as D/32 column blocks: the 64 rows
+// of elements [32c, 32c + 32) form a 4 KiB block, 64 bytes per row, and the
+// four 16-byte chunks q of row r sit at slot q ^ ((r >> 2) & 3). Both read
+// patterns are conflict-free: 16 consecutive rows at one chunk (the MFMA A
+// operand read row-wise) cover every 16-byte slot of 256 bytes once, and the
+// transposing reads (4 consecutive rows x 64 bytes per 32 lanes) 256
+// contiguous bytes. Every read of a wave then differs from one of four
+// per-lane offsets by a constant (see RowOff / TrOff).
+constexpr int kBlk = kTile * 64;  // bytes of one column block
 
+// direct-to-LDS loads of one tile: load j of the tile (1 KiB, LDS bytes
+// [1024j, +1024)) carries rows 16*(j%4) + lane/4 of column block j/4, the
+// lane's slot lane%4 holding logical chunk (lane%4) ^ (lane/16)
 template <int D>
-__device__ __forceinline__ int lds_off(int row, int elem) {
-  return row * (D * 2) + ((((elem >> 3) ^ swz<D>(row))) << 4) + ((elem & 7) << 1);
+__device__ __forceinline__ int tile_lane_offset(int lane) {
+  return (lane >> 2) * (D * 2) + ((((lane & 3) ^ (lane >> 4))) << 4);
 }
 
 // Loads of one 64-row tile (rows of 2*D bytes, contiguous from `tile`, of
-// which `bytes` are valid) into LDS `dst`: each of the 4 waves issues NI
-// 1 KiB direct-to-LDS loads; lane l of load i writes LDS bytes
-// (wave*NI + i)*1024 + 16*l, the physical chunk that the swizzle assigns to
-// the logical chunk the lane fetches. The resource starts at the tile and
-// ends after its valid bytes, and every offset is a per-lane (range-checked)
-// one, so rows past the end arrive as zeros.
+// which `bytes` are valid) into LDS `dst`: each of the 4 waves issues NI of
+// the tile's loads. The resource starts at the tile and ends after its valid
+// bytes, and every offset is a per-lane (range-checked) one, so rows past the
+// end arrive as zeros.
 template <int D>
 __device__ __forceinline__ void load_tile(const void* tile, long long bytes, char* dst, int wave,
                                           int lane) {
   constexpr int NI = kTile * D * 2 / (kWaves * 1024);
-  constexpr int kXorStep = (D == 128) ? 16 : 64;
-  static_assert((D == 128 && NI == 4) || (D == 64 && NI == 2),
-                "the per-load chunk flip assumes 4 (d=128) or 2 (d=64) loads per wave");
   const int range = (int)(bytes < 0 ? 0 : (bytes > kTile * D * 2 ? kTile * D * 2 : bytes));
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(tile), 0, range, kBufferFlags);
-  int lb = (D == 128) ? ((lane >> 4) * (D * 2)) | (16 * ((lane & 15) ^ (4 * (lane >> 4))))
-                      : ((lane >> 3) * (D * 2)) | (16 * ((lane & 7) ^ (lane >> 4)));
+  int lb = tile_lane_offset<D>(lane);
   asm volatile("" : "+v"(lb));
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(dst + (wave * NI + i) * 1024),
-                                             16, (lb ^ (kXorStep * i)) + (wave * NI + i) * 1024,
-                                             0, 0, 0);
+  for (int i = 0; i < NI; ++i) {
+    const int j = wave * NI + i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(dst + j * 1024), 16,
+                                             lb + 16 * (j & 3) * (D * 2) + 64 * (j >> 2), 0, 0,
+                                             0);
+  }
 }
 
-// Transposing read of a 32(d) x 16(row) A operand from a row-major tile: rows
-// r0, r0 + 8 (r0 already holds the lane's row within its group), columns col..
+// Per-lane offsets of the row-wise A-operand reads: lane l reads row
+// base + l%32, elements 16*dc + 8*(l/32) .. +8, at
+//   tile + off[dc % 2] + (dc / 2) * kBlk + base * 64      (base % 32 == 0)
+struct RowOff {
+  int off[2];
+};
+__device__ __forceinline__ RowOff row_offsets(int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  RowOff r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) r.off[h] = l32 * 64 + ((((2 * h + g) ^ ((l32 >> 2) & 3))) << 4);
+  return r;
+}
 template <int D>
-__device__ __forceinline__ bf16x8_t read_tr(const char* tile, int r0, int col) {
-  const i16x4_t lo =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4_t*)(tile + lds_off<D>(r0, col)));
+__device__ __forceinline__ bf16x8_t read_row(const char* tile, const RowOff& ro, int base,
+                                             int dc) {
+  return *reinterpret_cast<const bf16x8_t*>(tile + ro.off[dc & 1] + (dc >> 1) * kBlk + base * 64);
+}
+
+// Per-lane offsets of the transposing reads: a 32(d) x 16(row) A operand
+// from rows base + 16*hf + [4*(l/32) + (l%16)/4, +8] and columns
+// 32*db + [4*(l%4) + 16*((l/16)%2)] is
+//   tile + off[h] + db * kBlk + (base + 16*hf + 8*h) * 64   for the halves h = 0, 1
+struct TrOff {
+  int off[2];
+};
+__device__ __forceinline__ TrOff tr_offsets(int lane) {
+  const int g = lane >> 5, grp = lane >> 4, src = lane & 15;
+  const int tr_row = src >> 2;
+  const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
+  TrOff t;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    t.off[h] = (4 * g + tr_row) * 64 + (((((tr_col >> 3) & 3) ^ g ^ (2 * h))) << 4) +
+               ((tr_col & 7) << 1);
+  return t;
+}
+__device__ __forceinline__ bf16x8_t read_tr(const char* tile, const TrOff& to, int base, int hf,
+                                            int db) {
+  const char* p0 = tile + db * kBlk + (base + 16 * hf) * 64;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4_t*)(p0 + to.off[0]));
   const i16x4_t hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4_t*)(tile + lds_off<D>(r0 + 8, col)));
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4_t*)(p0 + 8 * 64 + to.off[1]));
   const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
   const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
   const u32x4_t a4 = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -219,52 +253,50 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
-  const int grp = lane >> 4;
-  const int src = lane & 15;
-  const int tr_row = src >> 2;
-  const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
+  const RowOff ro = row_offsets(lane);
+  const TrOff to = tr_offsets(lane);
 
-  auto tile_step = [&](int it, const char* kl, const char* vl) __attribute__((always_inline)) {
+  // One 64-key tile: Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ, dSᵀ = Pᵀ ∘ (dPᵀ − D), then
+  // dQᵀ += Kᵀ·dSᵀ. Only tiles that cross a row's last visible key (the causal
+  // diagonal, the ragged end) are MASKED.
+  auto tile_step = [&](auto masked_tag, int it, const char* kl, const char* vl)
+      __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = it * kTile;
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
-      dp[kb] = f32x16_t{};
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
-            kl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dc], s[kb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-            vl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[dc], dp[kb], 0, 0, 0);
-      }
-    }
-    const bool masked = k0 + kTile > mask_from || k0 + kTile > p.Nk;
-    // dSᵀ = Pᵀ ∘ (dPᵀ − D), packed to bf16 in Sᵀ register order
+    // per 32-key half: Sᵀ, dPᵀ, then dSᵀ = Pᵀ ∘ (dPᵀ − D) packed to bf16 in
+    // Sᵀ register order
     uint32_t pk[2][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      bf16x8_t ka[NDC];
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) ka[dc] = read_row<D>(kl, ro, kb * 32, dc);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], qf[dc], s, 0, 0, 0);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) ka[dc] = read_row<D>(vl, ro, kb * 32, dc);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[dc], df[dc], dp, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float e[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int i = 2 * j + h;
-          float x = s[kb][i];
-          if (masked) {
+          float x = s[i];
+          if (MASKED) {
             const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
             if (key > lim) x = neg_inf();
           }
           const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -lse2));
-          e[h] = pr * (dp[kb][i] - drow);
+          e[h] = pr * (dp[i] - drow);
         }
         pk[kb][j] = pack_bf16x2(e[0], e[1]);
       }
+    }
     // dQᵀ += Kᵀ dSᵀ, 16 keys per MFMA; Kᵀ through the transposing LDS read
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -273,30 +305,43 @@ void bwd_dq_kernel(BwdParams p) {
         const u32x4_t w4 = {pk[kb][4 * hf], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2],
                             pk[kb][4 * hf + 3]};
         const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, w4);
-        const int r0 = kb * 32 + 16 * hf + 4 * g + tr_row;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kl, r0, 32 * db + tr_col),
-                                                            bop, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(kl, to, kb * 32, hf, db), bop,
+                                                            acc[db], 0, 0, 0);
       }
+  };
+
+  // tiles before m0 hide no key from any row of the workgroup
+  const long long mlim = mask_from < (long long)p.Nk ? mask_from : (long long)p.Nk;
+  const int m0 = (int)(mlim / kTile);
+  // tile it (buffers it % 2, a compile-time choice): wait for it, free it-1's
+  // buffers, load it+1 into them, compute it
+  auto step = [&](auto buf_tag, int it) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    char* kc = BUF ? kb1 : kb0;
+    char* vc = BUF ? vb1 : vb0;
+    char* kn = BUF ? kb0 : kb1;
+    char* vn = BUF ? vb0 : vb1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it has landed
+    __syncthreads();                     // ... for every wave; tile it-1's buffers are free
+    if (it + 1 < ntiles) {
+      const long long t0 = (long long)(it + 1) * kTile * D;
+      load_tile<D>(p.k + kv_base + t0, kv_bytes - 2 * t0, kn, wave, lane);
+      load_tile<D>(p.v + kv_base + t0, kv_bytes - 2 * t0, vn, wave, lane);
+    }
+    if (it < m0)
+      tile_step(std::integral_constant<bool, false>{}, it, kc, vc);
+    else
+      tile_step(std::integral_constant<bool, true>{}, it, kc, vc);
   };
 
   if (ntiles > 0) {
     load_tile<D>(p.k + kv_base, kv_bytes, kb0, wave, lane);
     load_tile<D>(p.v + kv_base, kv_bytes, vb0, wave, lane);
-    for (int it = 0; it < ntiles; ++it) {
-      char* kc = (it & 1) ? kb1 : kb0;
-      char* vc = (it & 1) ? vb1 : vb0;
-      char* kn = (it & 1) ? kb0 : kb1;
-      char* vn = (it & 1) ? vb0 : vb1;
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it has landed
-      __syncthreads();                     // ... for every wave; tile it-1's buffers are free
-      if (it + 1 < ntiles) {
-        const long long t0 = (long long)(it + 1) * kTile * D;
-        load_tile<D>(p.k + kv_base + t0, kv_bytes - 2 * t0, kn, wave, lane);
-        load_tile<D>(p.v + kv_base + t0, kv_bytes - 2 * t0, vn, wave, lane);
-      }
-      tile_step(it, kc, vc);
+    for (int it = 0; it < ntiles; it += 2) {
+      step(std::integral_constant<int, 0>{}, it);
+      if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
     }
   }
 
@@ -351,8 +396,10 @@ void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char qbuf[3][TILE];
   __shared__ __attribute__((aligned(1024))) char obuf[3][TILE];  // dO tiles
   __shared__ __attribute__((aligned(16))) float lbuf[3][2 * kTile];  // base-2 LSE, then D
-  // P of a step, bf16 pairs in S register order: [buffer][slice][half][lane][8]
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf[2][kWaves][2][64][8];
+  // P of a step, bf16 pairs in S register order, the two 16-byte halves of a
+  // lane's 32 bytes in separate planes (lane-contiguous, conflict-free):
+  // [buffer][slice][query half qb][plane][lane]
+  __shared__ __attribute__((aligned(16))) u32x4_t pbuf[3][kWaves][2][2][64];
 
   const int tid = threadIdx.x;
   const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -397,20 +444,17 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16_t{};
 
-  const int grp = lane >> 4;
-  const int src = lane & 15;
-  const int tr_row = src >> 2;
-  const int tr_col = 4 * (src & 3) + 16 * (grp & 1);
   const int kq = my_key - p.q_offset;
+  const RowOff ro = row_offsets(lane);
+  const TrOff to = tr_offsets(lane);
 
   // step s's tiles into buffer s % 3, issued by the dV waves
-  auto issue = [&](int s) __attribute__((always_inline)) {
+  auto issue = [&](int s, int bi) __attribute__((always_inline)) {
     const int hq = kvh * p.G + split * gs + s / per_head;
     const int qt = qt_lo + s % per_head;
     const long long hbase = ((long long)b * p.Hq + hq) * (long long)p.Nq;
     const long long r0 = (long long)qt * kTile;
     const long long left = (long long)p.Nq - r0;
-    const int bi = s % 3;
     load_tile<D>(p.q + (hbase + r0) * D, left * D * 2, qbuf[bi], wave, lane);
     load_tile<D>(p.dout + (hbase + r0) * D, left * D * 2, obuf[bi], wave, lane);
     if (wave < 2) {
@@ -422,24 +466,25 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // dV role, step s: S, P (left in LDS for the dK wave), dVᵀ += dOᵀ P
-  auto step_v = [&](int s) __attribute__((always_inline)) {
-    const char* ql = qbuf[s % 3];
-    const char* ol = obuf[s % 3];
-    const float* ll = lbuf[s % 3];
+  // dV role, step s (buffers BI = s % 3): S, P (left in LDS for the dK wave),
+  // dVᵀ += dOᵀ P; only steps whose query rows reach below the slice's last
+  // key under a causal mask are MASKED
+  auto step_v = [&](auto masked_tag, auto buf_tag, int s) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int BI = decltype(buf_tag)::value;
+    const char* ql = qbuf[BI];
+    const char* ol = obuf[BI];
+    const float* ll = lbuf[BI];
     const int qrow0 = (qt_lo + s % per_head) * kTile;
-    // (decided at run time in both instantiations: with a compile-time false
-    // the non-causal schedule keeps more loads in flight and spills)
-    const bool masked = p.causal != 0 && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t sc = f32x16_t{};
+      bf16x8_t qa[NDC];
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(
-            ql + lds_off<D>(qb * 32 + l32, 16 * dc + 8 * g));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kv[dc], sc, 0, 0, 0);
-      }
+      for (int dc = 0; dc < NDC; ++dc) qa[dc] = read_row<D>(ql, ro, qb * 32, dc);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], sc, 0, 0, 0);
       uint32_t pk[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -448,45 +493,44 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float x = sc[4 * m + r];
-          if (masked && kq > qrow0 + qb * 32 + 8 * m + 4 * g + r) x = neg_inf();
+          if (MASKED && kq > qrow0 + qb * 32 + 8 * m + 4 * g + r) x = neg_inf();
           pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -l4[r]));
         }
         pk[2 * m] = pack_bf16x2(pv[0], pv[1]);
         pk[2 * m + 1] = pack_bf16x2(pv[2], pv[3]);
       }
-      uint32_t* pdst = pbuf[s & 1][wave][qb][lane];
-      *reinterpret_cast<u32x4_t*>(pdst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-      *reinterpret_cast<u32x4_t*>(pdst + 4) = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
+      pbuf[BI][wave][qb][0][lane] = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+      pbuf[BI][wave][qb][1][lane] = u32x4_t{pk[4], pk[5], pk[6], pk[7]};
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const u32x4_t w4 = {pk[4 * hf], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
         const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, w4);
-        const int r0 = qb * 32 + 16 * hf + 4 * g + tr_row;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ol, r0, 32 * db + tr_col),
-                                                            bo, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(ol, to, qb * 32, hf, db), bo,
+                                                            acc[db], 0, 0, 0);
       }
     }
   };
 
-  // dK role, step s (one step behind): dP, dS = P ∘ (dP − D), dKᵀ += Qᵀ dS
-  auto step_k = [&](int s) __attribute__((always_inline)) {
-    const char* ql = qbuf[s % 3];
-    const char* ol = obuf[s % 3];
-    const float* ll = lbuf[s % 3];
+  // dK role, step s (one step behind; buffers BI = s % 3): dP, dS = P ∘ (dP − D),
+  // dKᵀ += Qᵀ dS
+  auto step_k = [&](auto buf_tag) __attribute__((always_inline)) {
+    constexpr int BI = decltype(buf_tag)::value;
+    const char* ql = qbuf[BI];
+    const char* ol = obuf[BI];
+    const float* ll = lbuf[BI];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t dp = f32x16_t{};
+      bf16x8_t oa[NDC];
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const bf16x8_t oa = *reinterpret_cast<const bf16x8_t*>(
-            ol + lds_off<D>(qb * 32 + l32, 16 * dc + 8 * g));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, kv[dc], dp, 0, 0, 0);
-      }
-      const uint32_t* psrc = pbuf[s & 1][wave][qb][lane];
-      const u32x4_t p0 = *reinterpret_cast<const u32x4_t*>(psrc);
-      const u32x4_t p1 = *reinterpret_cast<const u32x4_t*>(psrc + 4);
+      for (int dc = 0; dc < NDC; ++dc) oa[dc] = read_row<D>(ol, ro, qb * 32, dc);
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dc], kv[dc], dp, 0, 0, 0);
+      const u32x4_t p0 = pbuf[BI][wave][qb][0][lane];
+      const u32x4_t p1 = pbuf[BI][wave][qb][1][lane];
       const uint32_t pp[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       uint32_t pd[8];
 #pragma unroll
@@ -504,26 +548,42 @@ void bwd_dkdv_kernel(BwdParams p) {
       for (int hf = 0; hf < 2; ++hf) {
         const u32x4_t w4 = {pd[4 * hf], pd[4 * hf + 1], pd[4 * hf + 2], pd[4 * hf + 3]};
         const bf16x8_t bo = __builtin_bit_cast(bf16x8_t, w4);
-        const int r0 = qb * 32 + 16 * hf + 4 * g + tr_row;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ql, r0, 32 * db + tr_col),
-                                                            bo, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr(ql, to, qb * 32, hf, db), bo,
+                                                            acc[db], 0, 0, 0);
       }
     }
   };
 
-  if (nsteps > 0) {
-    if (role == 0) issue(0);
-    for (int it = 0; it <= nsteps; ++it) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step it's tiles have landed
-      __syncthreads();  // ... for every wave; step it-2's buffers and it-1's P are handed over
-      if (role == 0) {
-        if (it + 1 < nsteps) issue(it + 1);
-        if (it < nsteps) step_v(it);
-      } else if (it >= 1) {
-        step_k(it - 1);
+  // Iteration it (R = it % 3, a compile-time choice after unrolling by 3):
+  // the dV waves load step it+1 into buffer (R+1) % 3 and compute step it
+  // from buffer R; the dK waves compute step it-1 from buffer (R+2) % 3.
+  auto iter = [&](auto r_tag, int it) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_tag)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step it's tiles have landed
+    __syncthreads();  // ... for every wave; step it-2's buffers and it-1's P are handed over
+    if (role == 0) {
+      if (it + 1 < nsteps) issue(it + 1, (R + 1) % 3);
+      if (it < nsteps) {
+        const int qrow0 = (qt_lo + it % per_head) * kTile;
+        const bool masked = p.causal != 0 && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
+        if (masked)
+          step_v(std::integral_constant<bool, true>{}, std::integral_constant<int, R>{}, it);
+        else
+          step_v(std::integral_constant<bool, false>{}, std::integral_constant<int, R>{}, it);
       }
+    } else if (it >= 1) {
+      step_k(std::integral_constant<int, (R + 2) % 3>{});
+    }
+  };
+
+  if (nsteps > 0) {
+    if (role == 0) issue(0, 0);
+    for (int it = 0; it <= nsteps; it += 3) {
+      iter(std::integral_constant<int, 0>{}, it);
+      if (it + 1 <= nsteps) iter(std::integral_constant<int, 1>{}, it + 1);
+      if (it + 2 <= nsteps) iter(std::integral_constant<int, 2>{}, it + 2);
     }
   }
 
