@@ -75,8 +75,8 @@ def parse():
                     help="skip the host-side 1000-chat block-pool simulation")
     ap.add_argument("--stage", default=None,
                     choices=["prefill_4k", "prefill_32k", "splitkv_decode_32k", "paged_decode_q4",
-                             "chunked_prefill_paged", "paged_decode_q4_fp8", "backward_4k",
-                             "single_head_f32", "copy_1gib"],
+                             "paged_decode_q4_d64", "chunked_prefill_paged", "paged_decode_q4_fp8",
+                             "backward_4k", "single_head_f32", "copy_1gib"],
                     help="run only this stage --steps times and exit (for profiler runs); "
                          "copy_1gib is a plain 1 GiB device copy used to calibrate HBM counters")
     return ap.parse_args()

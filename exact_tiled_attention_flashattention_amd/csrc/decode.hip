@@ -211,7 +211,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // K: token r16, 16 bytes at 16*g (+64 per further load); V: token 4*g (+jj
   // via soffset), the 8 d from 8*r16
   const int koff = r16 * rowb + 16 * g;
-  const int voff = (4 * g) * rowb + 8 * EB * r16;
+  // A V chunk holds 8 d; with D = 64 only lanes r16 < 8 have one inside the
+  // head, and the others take an offset past every range (zeros, no memory
+  // traffic) instead of the neighbouring head's bytes. Their PV outputs (d
+  // rows 64..127) are never stored.
+  const int voff = 8 * r16 < D ? (4 * g) * rowb + 8 * EB * r16 : 0x40000000;
   const int row = 16 * rg + r16;                // rows r = qi * G + h, r < M
   const bool row_ok = r16 < p.MP && row < p.M;
   const int qi = row_ok ? row / p.G : 0;

@@ -34,6 +34,10 @@ WORKLOADS = {
     # the paged 4-token decode over an E4M3 cache with per-head scales
     "paged_decode_q4_fp8": dict(seed=1007, kind="decode_paged_fp8", B=32, Hq=32, Hkv=8, Nq=4,
                                 d=128, len_lo=1024, len_hi=16384, dtype="bf16"),
+    # the paged 4-token decode at head dim 64 (its byte counters show that
+    # only the heads' own rows are read)
+    "paged_decode_q4_d64": dict(seed=1010, kind="decode_paged", B=32, Hq=32, Hkv=8, Nq=4, d=64,
+                                len_lo=1024, len_hi=16384, dtype="bf16"),
     # chunked prefill: a 512-token chunk per sequence appended after a cached
     # prefix, then attending to the whole paged cache
     "chunked_prefill_paged": dict(seed=1006, kind="prefill_paged", B=8, Hq=32, Hkv=8, Nq=512,
