@@ -479,22 +479,26 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t sc = f32x16_t{};
+      // every LDS read of the S chain and the softmax is issued before the MFMAs
       bf16x8_t qa[NDC];
+      f32x4_t l4[4];
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) qa[dc] = read_row<D>(ql, ro, qb * 32, dc);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        l4[m] = *reinterpret_cast<const f32x4_t*>(ll + qb * 32 + 8 * m + 4 * g);
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], sc, 0, 0, 0);
       uint32_t pk[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(ll + qb * 32 + 8 * m + 4 * g);
         float pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float x = sc[4 * m + r];
           if (MASKED && kq > qrow0 + qb * 32 + 8 * m + 4 * g + r) x = neg_inf();
-          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -l4[r]));
+          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -l4[m][r]));
         }
         pk[2 * m] = pack_bf16x2(pv[0], pv[1]);
         pk[2 * m + 1] = pack_bf16x2(pv[2], pv[3]);
@@ -523,24 +527,27 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t dp = f32x16_t{};
+      // every LDS read of the dP chain and of dS's other factors first
       bf16x8_t oa[NDC];
+      f32x4_t d4[4];
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) oa[dc] = read_row<D>(ol, ro, qb * 32, dc);
+      const u32x4_t p0 = pbuf[BI][wave][qb][0][lane];
+      const u32x4_t p1 = pbuf[BI][wave][qb][1][lane];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        d4[m] = *reinterpret_cast<const f32x4_t*>(ll + kTile + qb * 32 + 8 * m + 4 * g);
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dc], kv[dc], dp, 0, 0, 0);
-      const u32x4_t p0 = pbuf[BI][wave][qb][0][lane];
-      const u32x4_t p1 = pbuf[BI][wave][qb][1][lane];
       const uint32_t pp[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       uint32_t pd[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4_t d4 =
-            *reinterpret_cast<const f32x4_t*>(ll + kTile + qb * 32 + 8 * m + 4 * g);
-        const float e0 = bf16_lo(pp[2 * m]) * (dp[4 * m] - d4[0]);
-        const float e1 = bf16_hi(pp[2 * m]) * (dp[4 * m + 1] - d4[1]);
-        const float e2 = bf16_lo(pp[2 * m + 1]) * (dp[4 * m + 2] - d4[2]);
-        const float e3 = bf16_hi(pp[2 * m + 1]) * (dp[4 * m + 3] - d4[3]);
+        const float e0 = bf16_lo(pp[2 * m]) * (dp[4 * m] - d4[m][0]);
+        const float e1 = bf16_hi(pp[2 * m]) * (dp[4 * m + 1] - d4[m][1]);
+        const float e2 = bf16_lo(pp[2 * m + 1]) * (dp[4 * m + 2] - d4[m][2]);
+        const float e3 = bf16_hi(pp[2 * m + 1]) * (dp[4 * m + 3] - d4[m][3]);
         pd[2 * m] = pack_bf16x2(e0, e1);
         pd[2 * m + 1] = pack_bf16x2(e2, e3);
       }
