@@ -469,8 +469,7 @@ void bwd_dkdv_kernel(BwdParams p) {
   // dV role, step s (buffers BI = s % 3): S, P (left in LDS for the dK wave),
   // dVᵀ += dOᵀ P; only steps whose query rows reach below the slice's last
   // key under a causal mask are MASKED
-  auto step_v = [&](auto masked_tag, auto buf_tag, int s) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
+  auto step_v = [&](bool masked, auto buf_tag, int s) __attribute__((always_inline)) {
     constexpr int BI = decltype(buf_tag)::value;
     const char* ql = qbuf[BI];
     const char* ol = obuf[BI];
@@ -490,14 +489,19 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], sc, 0, 0, 0);
+      // a uniform branch around the masking alone keeps one copy of the step
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kq > qrow0 + qb * 32 + 8 * (i >> 2) + 4 * g + (i & 3)) sc[i] = neg_inf();
+      }
       uint32_t pk[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         float pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = sc[4 * m + r];
-          if (MASKED && kq > qrow0 + qb * 32 + 8 * m + 4 * g + r) x = neg_inf();
+          const float x = sc[4 * m + r];
           pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.c, -l4[m][r]));
         }
         pk[2 * m] = pack_bf16x2(pv[0], pv[1]);
@@ -563,34 +567,54 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   };
 
-  // Iteration it (R = it % 3, a compile-time choice after unrolling by 3):
-  // the dV waves load step it+1 into buffer (R+1) % 3 and compute step it
-  // from buffer R; the dK waves compute step it-1 from buffer (R+2) % 3.
-  auto iter = [&](auto r_tag, int it) __attribute__((always_inline)) {
-    constexpr int R = decltype(r_tag)::value;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step it's tiles have landed
-    __syncthreads();  // ... for every wave; step it-2's buffers and it-1's P are handed over
-    if (role == 0) {
-      if (it + 1 < nsteps) issue(it + 1, (R + 1) % 3);
-      if (it < nsteps) {
-        const int qrow0 = (qt_lo + it % per_head) * kTile;
-        const bool masked = p.causal != 0 && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
-        if (masked)
-          step_v(std::integral_constant<bool, true>{}, std::integral_constant<int, R>{}, it);
-        else
-          step_v(std::integral_constant<bool, false>{}, std::integral_constant<int, R>{}, it);
-      }
-    } else if (it >= 1) {
-      step_k(std::integral_constant<int, (R + 2) % 3>{});
-    }
+  // Barrier n: step n's tiles have landed and every wave is past step n-1
+  // (n = 0 .. nsteps). After it the dV waves load step n+1 into buffer
+  // (n+1) % 3 and compute step n from buffer n % 3; the dK waves compute step
+  // n-1. Each role runs its own loop, unrolled by three so that every buffer
+  // index is a compile-time constant, with the same barrier count; the
+  // remainder of fewer than three steps is peeled.
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed
+    __syncthreads();
   };
+  auto v_iter = [&](auto r_tag, int it) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_tag)::value;
+    barrier();
+    if (it + 1 < nsteps) issue(it + 1, (R + 1) % 3);
+    const int qrow0 = (qt_lo + it % per_head) * kTile;
+    const bool masked = p.causal != 0 && (long long)qrow0 + p.q_offset < (long long)kw0 + 31;
+    step_v(masked, r_tag, it);
+  };
+  auto k_iter = [&](auto r_tag) __attribute__((always_inline)) {
+    barrier();
+    step_k(r_tag);
+  };
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
 
   if (nsteps > 0) {
-    if (role == 0) issue(0, 0);
-    for (int it = 0; it <= nsteps; it += 3) {
-      iter(std::integral_constant<int, 0>{}, it);
-      if (it + 1 <= nsteps) iter(std::integral_constant<int, 1>{}, it + 1);
-      if (it + 2 <= nsteps) iter(std::integral_constant<int, 2>{}, it + 2);
+    if (role == 0) {
+      issue(0, 0);
+      int it = 0;
+      for (; it + 3 <= nsteps; it += 3) {
+        v_iter(R0{}, it);
+        v_iter(R1{}, it + 1);
+        v_iter(R2{}, it + 2);
+      }
+      if (it < nsteps) v_iter(R0{}, it);
+      if (it + 1 < nsteps) v_iter(R1{}, it + 1);
+      barrier();  // barrier nsteps: the dK waves' last step
+    } else {
+      barrier();  // barrier 0: nothing to do yet
+      int j = 0;
+      for (; j + 3 <= nsteps; j += 3) {
+        k_iter(R0{});
+        k_iter(R1{});
+        k_iter(R2{});
+      }
+      if (j < nsteps) k_iter(R0{});
+      if (j + 1 < nsteps) k_iter(R1{});
     }
   }
 
