@@ -78,6 +78,18 @@ __device__ __forceinline__ int seq_steps(const DecodeParams& p, int b) {
   return (cache_len_clamped(p.cv, p.seq_lens[b]) + 31) >> 5;
 }
 
+// A value every lane of the wave holds alike, moved to scalar registers. The
+// compiler cannot prove that values read from memory with a uniform address,
+// or taken out of a shuffle, are uniform; without this, the buffer resources
+// built from them live in vector registers and every load gets a loop over
+// lanes around it.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ long long uniform(long long x) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(x & 0xffffffffLL));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+  return ((long long)hi << 32) | (unsigned)lo;
+}
+
 __device__ __forceinline__ long long wave_sum64(long long x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
@@ -179,6 +191,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     tot += __shfl(incl, 63, 64);
   }
+  tot = uniform(tot);
   // at most one wave per step, so every wave's range is non-empty and the
   // pieces of a sequence come from consecutive waves with no gap
   const int We = (int)min((long long)p.Wh, tot);
@@ -204,7 +217,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       run += __shfl(incl, 63, 64);
     }
   }
-  b = __builtin_amdgcn_readfirstlane(b);
+  b = uniform(b);
+  pb = uniform(pb);
 
   const int rowb = p.cv.hkv * D * EB;  // bytes between consecutive tokens of one head
   // loop-invariant lane byte offsets inside a 16-token stretch
@@ -456,19 +470,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
 
   // ---- walk the sequences that [x0, x1) covers ---------------------------------
-  int st_b = seq_steps(p, b);
+  int st_b = uniform(seq_steps(p, b));
   long long seg = pb;  // first step of sequence b
   long long x = x0;
   while (x < x1) {
     const int lo = (int)(x - seg);
     const int hi = (int)min((long long)st_b, x1 - seg);
-    const int n = cache_len_clamped(p.cv, p.seq_lens[b]);
+    const int n = uniform(cache_len_clamped(p.cv, p.seq_lens[b]));
     piece(b, kvh, n, 32 * lo, min(n, 32 * hi), (long long)vh * (p.Wh + p.B) + j + b);
     x = seg + hi;
     seg += st_b;
     do {
       ++b;
-      st_b = b < p.B ? seq_steps(p, b) : 1;
+      st_b = b < p.B ? uniform(seq_steps(p, b)) : 1;
     } while (b < p.B && st_b == 0);
   }
 }
