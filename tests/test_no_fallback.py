@@ -32,6 +32,8 @@ def test_every_entry_point_raises_without_the_library(no_library):
         lambda: eta.kv_append_fp8(qd, qd, cache, cache, lse, lse, sl),
         lambda: eta.attn_gather_paged(cache, sl),
         lambda: eta.attn_decode_workspace_bytes(1, 2, 1, 1, 64, 16),
+        lambda: eta.attn_decode_paged_noalloc(qd, cache, cache, sl),
+        lambda: eta.attn_prefill_workgroup_waves(1, 2, 1, 4, True),
         lambda: eta.BlockPool(4),
     ]
     for call in calls:
