@@ -45,6 +45,9 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTile = 64;                  // rows per streamed tile
 constexpr int kBufferFlags = 0x00020000;   // raw buffer resource, 32-bit dword data
+// sched_barrier mask: VALU, SALU and transcendental instructions may be
+// scheduled across it; LDS reads and MFMAs may not
+constexpr int kSchedAluOnly = 0x406;
 
 struct BwdParams {
   const __bf16* q;
@@ -486,6 +489,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         l4[m] = *reinterpret_cast<const f32x4_t*>(ll + qb * 32 + 8 * m + 4 * g);
+      // the chain's reads all issue before its first MFMA (VALU/SALU may cross)
+      __builtin_amdgcn_sched_barrier(kSchedAluOnly);
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[dc], kv[dc], sc, 0, 0, 0);
@@ -541,6 +546,8 @@ void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         d4[m] = *reinterpret_cast<const f32x4_t*>(ll + kTile + qb * 32 + 8 * m + 4 * g);
+      // the chain's reads all issue before its first MFMA (VALU/SALU may cross)
+      __builtin_amdgcn_sched_barrier(kSchedAluOnly);
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[dc], kv[dc], dp, 0, 0, 0);

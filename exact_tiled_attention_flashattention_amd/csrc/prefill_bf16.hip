@@ -43,6 +43,9 @@ namespace {
 constexpr int kBN = 64;         // keys per tile
 constexpr float kTau = 8.0f;    // rescale only when a row max grows by more than 2^8
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, 32-bit dword data
+// sched_barrier mask: VALU, SALU and transcendental instructions may be
+// scheduled across it; LDS reads and MFMAs may not
+constexpr int kSchedAluOnly = 0x406;
 
 struct PrefillParams {
   const __bf16* q;
@@ -362,15 +365,25 @@ void prefill_bf16_kernel(PrefillParams p) {
 
   // Sᵀ[key][row] of one tile: two 32-key halves, K (A operand) from LDS
   auto scores = [&](const char* kl, f32x16_t (&s)[2]) {
+    // Each K operand read is issued four MFMAs before the MFMA that takes it;
+    // the scheduling barriers keep that order (VALU and SALU work may still
+    // move across them)
+    constexpr int NM = 2 * NDC;
+    constexpr int LA = 4;
+    bf16x8_t a[NM];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8_t*>(
+          kl + lds_off<D>((i / NDC) * 32 + l32, 16 * (i % NDC) + 8 * g));
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
+    for (int i = 0; i < LA; ++i) a[i] = rd(i);
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            kl + lds_off<D>(kb * 32 + l32, 16 * dc + 8 * g));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[dc], s[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < NM; ++i) {
+      if (i + LA < NM) a[i + LA] = rd(i + LA);
+      __builtin_amdgcn_sched_barrier(kSchedAluOnly);
+      s[i / NDC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qf[i % NDC], s[i / NDC], 0, 0, 0);
     }
   };
   // only tiles past the first row's diagonal, the ragged end or a missing
