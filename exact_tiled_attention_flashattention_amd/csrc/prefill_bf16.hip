@@ -264,91 +264,80 @@ void prefill_bf16_kernel(PrefillParams p) {
 
   // Token-major cache: a 64-key tile is four 16-token blocks; each block is
   // loaded by two waves (8 rows each) through a resource that ends after the
-  // block's last valid row. The blocks are looked up through a window of 64
-  // consecutive logical blocks held one per lane: the element offset of the
-  // block's head-kvh rows in the pool (64-bit), and two masks, `wst` (the
-  // block has storage) and `wok` (it has storage or lies past the sequence,
-  // where position masks its keys anyway). A tile's lookup is then a
-  // readlane and a shift; the window is refilled every 14 tiles, its table
-  // entries loaded one step before they are needed.
+  // block's last valid row. A tile's four block-table entries arrive by one
+  // vector load (lane l holds the entry of block 4t + l%4) a step before the
+  // tile's K is loaded, so they have landed at the step's load wait; the
+  // wave's own entry is then a readlane and the tile's storage bits a ballot.
+  // Entries past the table row clamp to its last one: those blocks lie past
+  // the sequence (nk <= 16 * max_blocks), and position hides their keys.
   const int rowb = p.Hkv * D * 2;  // bytes between consecutive tokens of one head
-  int wbase = -(1 << 30);          // first logical block of the window
-  int woff_lo = 0, woff_hi = 0;    // this lane's block offset in elements
-  unsigned long long wst = 0, wok = 0;
-  int nbase = -(1 << 30), nent = -1;  // the next window: first block, this lane's table entry
-  auto fetch = [&](int base) {
-    nbase = base;
-    const int i = base + lane;
-    if (p.table != nullptr)
-      nent = i < p.max_blocks ? p.table[(long long)b * p.max_blocks + i] : -1;
-    else
-      nent = i;
+  // A contiguous cache has no table: its block jb of sequence b starts at
+  // element b * max_len * Hkv * D + jb * 16 * Hkv * D, a pool block e at
+  // e * 16 * Hkv * D, so both are `seq_base + e * blk_elems` with e the
+  // table entry or jb. Without a table the entry loads read seq_lens[0]
+  // instead (any valid address; the value is unused), so they need no branch.
+  const bool paged = p.table != nullptr;
+  const long long blk_elems = (long long)kBlockTokens * p.Hkv * D;
+  const long long seq_base =
+      (paged ? 0 : (long long)b * p.max_len * p.Hkv * D) + (long long)kvh * D;
+  const int* const trow = paged ? p.table + (long long)b * p.max_blocks : p.seq_lens;
+  const int tlast = paged ? max(p.max_blocks - 1, 0) : 0;
+  // entries of blocks 4t + l%4 (lane l), or of blocks 4t0 + l for the first tiles
+  auto load_ents = [&](int first_block, int span) __attribute__((always_inline)) {
+    return trow[min(first_block + lane % span, tlast)];
   };
-  auto install = [&]() {
-    wbase = nbase;
-    const int i = wbase + lane;
-    const bool ok = p.table != nullptr ? (nent >= 0 && nent < p.num_blocks) : true;
-    const bool past = nk - kBlockTokens * i <= 0;
-    const long long off =
-        !ok ? 0
-            : p.table != nullptr
-                  ? ((long long)nent * kBlockTokens * p.Hkv + kvh) * D
-                  : (((long long)b * p.max_len + (long long)kBlockTokens * i) * p.Hkv + kvh) * D;
-    woff_lo = (int)(off & 0xffffffffLL);
-    woff_hi = (int)(off >> 32);
-    wst = __builtin_amdgcn_ballot_w64(ok);
-    wok = __builtin_amdgcn_ballot_w64(ok || past);
+  // block jb's storage: the pool entry `ent` (paged) or its place in the
+  // contiguous cache; no storage (or no valid row) gives an empty range
+  auto block_stored = [&](int ent) __attribute__((always_inline)) {
+    return !paged || (unsigned)ent < (unsigned)p.num_blocks;
   };
-  // make the window cover tile t (called for t = 0, 1, 2, ... in order), and
-  // fetch the next window when tile t+1 would leave this one
-  auto window_for = [&](int t) __attribute__((always_inline)) {
-    if (4 * t + 3 >= wbase + 64) {
-      if (!(nbase <= 4 * t && 4 * t + 3 < nbase + 64)) fetch(max(0, 4 * t - 8));
-      install();
-    }
-    if (4 * t + 7 >= wbase + 64) fetch(max(0, 4 * t - 4));
-  };
-  auto block_rsrc = [&](const __bf16* pool, int jb) __attribute__((always_inline)) {
-    const int i = jb - wbase;
-    const long long off = ((long long)__builtin_amdgcn_readlane(woff_hi, i) << 32) |
-                          (unsigned)__builtin_amdgcn_readlane(woff_lo, i);
+  auto block_rsrc = [&](const __bf16* pool, int jb, int ent) __attribute__((always_inline)) {
     const int valid = min(kBlockTokens, nk - kBlockTokens * jb);
-    const bool ok = ((wst >> i) & 1ull) != 0 && valid > 0;
+    const bool ok = block_stored(ent) && valid > 0;
+    const long long off = seq_base + (long long)(paged ? ent : jb) * blk_elems;
     return __builtin_amdgcn_make_buffer_rsrc(
         (void*)(pool + (ok ? off : 0)), 0, ok ? (valid - 1) * rowb + D * 2 : 0, kBufferFlags);
   };
   // the waves split the tile's four 16-token blocks evenly, WB = waves per block
   constexpr int WB = kWaves / 4;
-  auto load_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
+  const int wq = wave / WB;  // this wave's block of a tile
+  auto load_block = [&](const __bf16* pool, int t, int ent, char* dst)
+      __attribute__((always_inline)) {
     // K: wave w loads rows [16/WB*(w%WB), +16/WB) of block 4t + w/WB
-    load_rows(block_rsrc(pool, 4 * t + wave / WB), (wave % WB) * (kBlockTokens / WB) * rowb,
-              rowb, dst);
+    load_rows(block_rsrc(pool, 4 * t + wq, ent), (wave % WB) * (kBlockTokens / WB) * rowb, rowb,
+              dst);
   };
-  auto load_v_block = [&](const __bf16* pool, int t, char* dst) __attribute__((always_inline)) {
+  auto load_v_block = [&](const __bf16* pool, int t, int ent, char* dst)
+      __attribute__((always_inline)) {
     // V: wave w loads column blocks [NI*(w%WB), +NI) of block q = w/WB, the
     // block's 16 rows of each (LDS bytes 1024*q of the column block)
-    const int q = wave / WB;
-    const __amdgpu_buffer_rsrc_t rs = block_rsrc(pool, 4 * t + q);
+    const __amdgpu_buffer_rsrc_t rs = block_rsrc(pool, 4 * t + wq, ent);
     int lb = (lane >> 2) * rowb + 16 * (lane & 3);
     asm volatile("" : "+v"(lb));
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int db = (wave % WB) * NI + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (ATTN_LDS void*)(dst + db * kVBlockBytes + q * 1024), 16, lb, 64 * db, 0, 0);
+          rs, (ATTN_LDS void*)(dst + db * kVBlockBytes + wq * 1024), 16, lb, 64 * db, 0, 0);
     }
   };
-  // bit q: block 4t + q of tile t has storage (blocks past the sequence count
-  // as present; their keys are masked by position)
-  auto tile_ok_bits = [&](int t) -> unsigned {
-    return (unsigned)(wok >> (4 * t - wbase)) & 0xFu;
+  // lanes [l0, l0 + 4) of `ents` hold tile t's entries: bit q = block 4t + q
+  // has storage (blocks past the sequence count as present; their keys are
+  // masked by position)
+  auto tile_ok_bits = [&](int t, int ents, int l0) -> unsigned {
+    const int jb = 4 * t + lane - l0;
+    const bool ok = block_stored(ents) || nk - kBlockTokens * jb <= 0;
+    return (unsigned)(__builtin_amdgcn_ballot_w64(ok) >> l0) & 0xFu;
   };
+  int vk = 0;         // lanes 0..3: entries of the tile whose K is loaded next
+  int ent_v = 0;      // this wave's entry of the tile whose V is loaded next
   // tile t's K, V into LDS; issue_k returns the tile's block bits (cache)
   auto issue_k = [&](int t, char* dst) __attribute__((always_inline)) -> unsigned {
     if constexpr (CACHE) {
-      window_for(t);
-      load_block(p.k, t, dst);
-      return tile_ok_bits(t);
+      // vk holds tile t's entries in lanes 0..3
+      const int ent = __builtin_amdgcn_readlane(vk, wq);
+      load_block(p.k, t, ent, dst);
+      return tile_ok_bits(t, vk, 0);
     } else {
       load_rows(krs, t * kBN * D * 2 + wave * NI * 1024, D * 2, dst);
       return 0xFu;
@@ -356,7 +345,7 @@ void prefill_bf16_kernel(PrefillParams p) {
   };
   auto issue_v = [&](int t, char* dst) __attribute__((always_inline)) {
     if constexpr (CACHE)
-      load_v_block(p.v, t, dst);
+      load_v_block(p.v, t, ent_v, dst);
     else
       load_v_rows(vrs, t * kBN * D * 2, D * 2, dst);
   };
@@ -447,9 +436,17 @@ void prefill_bf16_kernel(PrefillParams p) {
     const int k0 = it * kBN;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(it+1) and V(it) have landed
     __syncthreads();                     // ... for every wave; the free buffers are free
+    // (cache) the table entries loaded last step are read only after the wait
+    if constexpr (CACHE) asm volatile("" : "+v"(vk));
     if (!LAST) {
+      int ent_k = 0;
+      if constexpr (CACHE) ent_k = __builtin_amdgcn_readlane(vk, wq);  // tile it+2
       if (it + 2 < ntiles) okq |= issue_k(it + 2, kfree) << 8;
       issue_v(it + 1, vfree);
+      if constexpr (CACHE) {
+        ent_v = ent_k;
+        if (it + 3 < ntiles) vk = load_ents(4 * (it + 3), 4);
+      }
     }
     if (needs_mask(k0)) {
       mask(k0, sc);
@@ -518,9 +515,26 @@ void prefill_bf16_kernel(PrefillParams p) {
   };
 
   if (ntiles > 0) {
-    okq = issue_k(0, kb0);
-    issue_v(0, vb0);
-    if (ntiles > 1) okq |= issue_k(1, kb1) << 4;
+    if constexpr (CACHE) {
+      // the entries of tiles 0..2 (lanes 0..11), before any tile load
+      const int e3 = load_ents(0, 12);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      vk = e3;
+      ent_v = __builtin_amdgcn_readlane(e3, wq);
+      load_block(p.k, 0, ent_v, kb0);
+      okq = tile_ok_bits(0, e3, 0);
+      issue_v(0, vb0);
+      if (ntiles > 1) {
+        ent_v = __builtin_amdgcn_readlane(e3, 4 + wq);
+        load_block(p.k, 1, ent_v, kb1);
+        okq |= tile_ok_bits(1, e3, 4) << 4;
+      }
+      vk = __shfl(e3, 8 + (lane & 3), 64);  // tile 2's entries to lanes 0..3
+    } else {
+      okq = issue_k(0, kb0);
+      issue_v(0, vb0);
+      if (ntiles > 1) okq |= issue_k(1, kb1) << 4;
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     f32x16_t sa[2], sb[2];
