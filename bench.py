@@ -183,19 +183,30 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters_all_workload
 CSRC = os.path.join(ROOT, "exact_tiled_attention_flashattention_amd", "csrc")
 
 
+def source_fingerprint(sources):
+    """First 16 hex digits of the sha256 of the kernel sources' code: comments and
+    blank lines are dropped, so that a change of wording alone keeps the figure."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for f in sources:
+        with open(os.path.join(CSRC, f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code.strip():
+                h.update((code + "\n").encode())
+    return h.hexdigest()[:16]
+
+
 def counter_traffic(stage, kernel, sources):
     """HBM bytes per launch of `kernel` on `stage` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy calibration), or None
-    when the kernel's sources have changed since the counters were taken."""
-    import hashlib
-
+    when the kernel's code has changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    h = hashlib.sha256()
-    for f in sources:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    fp = h.hexdigest()[:16]
+    fp = source_fingerprint(sources)
     with open(TRAFFIC_FILE) as fh:
         for line in fh:
             parts = line.split()

@@ -23,10 +23,13 @@
 //     and row sum need one cross-half exchange (permlane32 swap).
 //   * The probabilities in the Sᵀ accumulator layout are already the B
 //     operand (Pᵀ) of Oᵀ = Vᵀ·Pᵀ after a bf16 pack; Vᵀ comes straight out of
-//     the row-major V tile in LDS through the transposing read
-//     ds_read_tr16_b64. Oᵀ stays in 64 fp32 accumulators per lane.
-//   * K/V tiles (64 keys) are double-buffered: the next tile's global loads
-//     are in flight while the current one is computed.
+//     the V tile in LDS (stored as 64-byte column blocks) through the
+//     transposing read ds_read_tr16_b64. Oᵀ stays in 64 fp32 accumulators
+//     per lane.
+//   * K/V tiles (64 keys) arrive by direct global-to-LDS loads into two
+//     buffers each: K runs two tiles ahead of the PV product, V one, so the
+//     loads are in flight while the current tile is computed. A cached K/V
+//     tile is four 16-token blocks found through the block table.
 //   * Softmax runs in base 2 with scale·log2(e) folded into one FMA.
 //   * Causal workgroups are launched longest-first (highest query block
 //     first) and skip every tile past their last row's diagonal; only tiles
