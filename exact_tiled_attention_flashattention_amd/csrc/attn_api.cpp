@@ -36,7 +36,7 @@ int device_compute_units() {
 namespace {
 
 constexpr int kWavesPerCu = 4;          // default bf16-cache decode workers per CU (one per SIMD)
-constexpr int kWavesPerCuFp8 = 8;       // default fp8-cache decode workers per CU (two per SIMD)
+constexpr int kWavesPerCuFp8 = 4;       // default fp8-cache decode workers per CU (one per SIMD)
 constexpr int kMaxWorkers = 1 << 20;
 constexpr int kMaxRows = 64;            // G*Nq rows per K/V head (four groups of 16)
 
@@ -46,10 +46,10 @@ bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
-// Default number of decode workers: one per SIMD of the current device for a
-// bf16 cache; two per SIMD for an fp8 cache, whose per-byte widening work
-// needs a second wave to keep the same bytes in flight (measured: 127 us
-// against 150 us for the paged 4-token workload).
+// Default number of decode workers: one per SIMD of the current device, for
+// either cache format (the paged 4-token workload over an fp8 cache, on one
+// MI355X: 122.5-124.5 us with one wave per SIMD, 126.7-126.9 us with two, and
+// 137-144 us for counts that are not a multiple of the SIMD count).
 int default_workers(bool kv8) {
   return attn::device_compute_units() * (kv8 ? kWavesPerCuFp8 : kWavesPerCu);
 }

@@ -143,7 +143,7 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
  *                 sequences are laid end to end and cut into that many equal
  *                 ranges, so the split adapts to ragged lengths. 0 picks a
  *                 default for the current device: one worker per SIMD (four
- *                 per compute unit) here, two per SIMD for the fp8 cache.
+ *                 per compute unit), for either cache format.
  *   workspace   : device scratch of at least attn_decode_workspace_bytes()
  *                 bytes for the same arguments, owned by the caller and
  *                 free again once the call's work on `stream` is done. It
