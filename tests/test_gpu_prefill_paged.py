@@ -133,6 +133,34 @@ def test_nan_in_unused_cache_rows_does_not_leak():
     check(o, O, lse, L, "bf16", "poisoned pool")
 
 
+@pytest.mark.parametrize("cache_lens,waves", [
+    ((60, 30), 8), ((60, 30), 4),   # 5 and 4 blocks: the longest row ends 3 blocks into a tile
+    ((92, 8, 40), 8),               # 7, 2 and 4 blocks
+])
+def test_table_row_ends_inside_a_tile(cache_lens, waves):
+    """A tile's four table entries are read as one group; where the table row ends
+    inside the last tile the reads past it stay inside the row and those blocks
+    (past the sequence) hide nothing and read nothing: NaN in every block the
+    table does not name must not reach the output."""
+    dev = need_gpu()
+    B = len(cache_lens)
+    announce(f"paged prefill, table rows ending inside a tile, cached {cache_lens}, "
+             f"Nq=20, waves={waves}")
+    inp = inputs.paged_inputs(35, B, 8, 2, 20, 128, 0, 0, spare_blocks=8, cache_lens=cache_lens)
+    kp = oracle.kv_append_ref(inp["k_pool"], inp["k_new"], inp["block_table"], inp["cache_lens"])
+    vp = oracle.kv_append_ref(inp["v_pool"], inp["v_new"], inp["block_table"], inp["cache_lens"])
+    inp["k_pool"], inp["v_pool"] = kp, vp
+    assert inputs.poison_unused(inp) > 0
+    assert inp["block_table"].shape[1] % 4 != 0
+    g = _dev(inp, dev)
+    o, lse = eta.attn_prefill_paged(g["q"], g["k_pool"], g["v_pool"], g["seq_lens"],
+                                    block_table=g["block_table"], causal=True, waves=waves)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_attention(inp["q"], kp, vp, inp["seq_lens"], scale_of(128), True,
+                                   block_table=inp["block_table"])
+    check(o, O, lse, L, "bf16", "table row ends inside a tile")
+
+
 def test_prompt_in_chunks_matches_full_prefill():
     """A 700-token prompt processed as chunks of 256, 256, 188 (kv_append, then
     attention against the paged cache) gives the rows of one causal prefill."""
