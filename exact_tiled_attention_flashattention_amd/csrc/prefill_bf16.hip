@@ -359,13 +359,15 @@ void prefill_bf16_kernel(PrefillParams p) {
   auto scores = [&](const char* kl, f32x16_t (&s)[2]) {
     // Each K operand read is issued four MFMAs before the MFMA that takes it;
     // the scheduling barriers keep that order (VALU and SALU work may still
-    // move across them)
+    // move across them). The two 32-key halves' accumulation chains
+    // alternate (MFMA i adds k-step i/2 to half i%2), so no MFMA waits on the
+    // one just issued; each half still sums its k-steps in order.
     constexpr int NM = 2 * NDC;
     constexpr int LA = 4;
     bf16x8_t a[NM];
     auto rd = [&](int i) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8_t*>(
-          kl + lds_off<D>((i / NDC) * 32 + l32, 16 * (i % NDC) + 8 * g));
+          kl + lds_off<D>((i & 1) * 32 + l32, 16 * (i >> 1) + 8 * g));
     };
 #pragma unroll
     for (int i = 0; i < LA; ++i) a[i] = rd(i);
@@ -375,7 +377,7 @@ void prefill_bf16_kernel(PrefillParams p) {
     for (int i = 0; i < NM; ++i) {
       if (i + LA < NM) a[i + LA] = rd(i + LA);
       __builtin_amdgcn_sched_barrier(kSchedAluOnly);
-      s[i / NDC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qf[i % NDC], s[i / NDC], 0, 0, 0);
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qf[i >> 1], s[i & 1], 0, 0, 0);
     }
   };
   // only tiles past the first row's diagonal, the ragged end or a missing
