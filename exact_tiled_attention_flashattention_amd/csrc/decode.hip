@@ -19,10 +19,10 @@
 //     equal contiguous range of them, so the load stays balanced whatever the
 //     sequence lengths. Wave w serves head w % Hkv, so the waves resident
 //     side by side read the same token rows of every head. A wave writes one
-//     partial result per sequence piece it covers; the piece of the head's
-//     wave j in sequence b lives at index kvh*(Wh + B) + j + b, which is
-//     unique. With fewer steps than waves only the first (number of steps)
-//     waves of a head run.
+//     partial result per sequence piece it covers; the piece of wave j of
+//     (K/V head, row group) vh in sequence b lives at index vh*(Wh + B) + j + b,
+//     which is unique. With fewer steps than waves only the first (number of
+//     steps) waves of a head run.
 //   * The G·Nq query rows that share a K/V head (G = Hq/Hkv query heads ×
 //     Nq new tokens, up to 64) are cut into groups of 16, each group the 16
 //     columns of v_mfma_f32_16x16x32_bf16: a K/V byte is loaded once per
