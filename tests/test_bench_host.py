@@ -37,3 +37,33 @@ def test_counter_traffic_is_null_for_other_sources():
     assert bench.counter_traffic("prefill_4k", "prefill_bf16_kernel<128,true,false>",
                                  ["common.h", "kv_cache.hip"]) is None
     assert bench.counter_traffic("no_such_stage", "x", ["common.h"]) is None
+
+
+def test_fingerprint_covers_code_not_comments(tmp_path, monkeypatch):
+    base = "// a kernel\nint f(int x) {\n  return x + 1;  // add one\n}\n"
+    (tmp_path / "a.hip").write_text(base)
+    (tmp_path / "b.hip").write_text("/* reworded\n   header */\n// other words\n\nint f(int x) {\n"
+                                    "  return x + 1;  // plus one\n\n}\n")
+    (tmp_path / "c.hip").write_text(base.replace("x + 1", "x + 2"))
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    fa = bench.source_fingerprint(["a.hip"])
+    assert fa == bench.source_fingerprint(["b.hip"])
+    assert fa != bench.source_fingerprint(["c.hip"])
+    assert len(fa) == 16
+
+
+def test_counter_traffic_reads_only_a_matching_fingerprint(tmp_path, monkeypatch):
+    (tmp_path / "k.hip").write_text("int k() { return 3; }\n")
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    fp = bench.source_fingerprint(["k.hip"])
+    summary = tmp_path / "traffic.md"
+    summary.write_text(
+        "# notes\n"
+        f"traffic st kern<1,2> bytes_per_launch=1234 read_bytes=1000 write_bytes=234 sources_sha256={fp}\n"
+        "traffic st other bytes_per_launch=9 read_bytes=9 write_bytes=0 sources_sha256=0000\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(summary))
+    assert bench.counter_traffic("st", "kern<1,2>", ["k.hip"]) == 1234
+    assert bench.counter_traffic("st", "other", ["k.hip"]) is None  # stale fingerprint
+    assert bench.counter_traffic("st2", "kern<1,2>", ["k.hip"]) is None
+    (tmp_path / "k.hip").write_text("int k() { return 4; }\n")  # the kernel changed
+    assert bench.counter_traffic("st", "kern<1,2>", ["k.hip"]) is None
