@@ -41,6 +41,9 @@ def _dev(inp, dev):
     (3, 8, 2, 5, 128, 5, 200, True, 0),       # G=4, Nq=5: 20 rows, ragged second group
     (2, 2, 2, 64, 128, 64, 400, True, 0),     # G=1, Nq=64: 64 query tokens, causal offsets
     (2, 32, 8, 8, 128, 50, 500, False, 3),    # G=4, Nq=8: 32 rows, not causal
+    # more sequences than a wave's 64 lanes: the range search scans B in passes of 64
+    (130, 8, 2, 1, 64, 1, 80, True, 0),
+    (130, 8, 2, 4, 128, 10, 200, True, 333),
 ])
 def test_paged_small(B, Hq, Hkv, Nq, d, lo, hi, causal, splits):
     dev = need_gpu()
