@@ -90,6 +90,7 @@ def _reference(inp, causal, d):
     (4, 4, 4, 8, 128, 1, 70, False, 1),
     (2, 32, 4, 4, 128, 100, 700, True, 0),    # 32 rows per K/V head: two groups
     (2, 16, 1, 4, 64, 40, 300, True, 5),      # 64 rows, four groups
+    (130, 8, 2, 4, 128, 10, 120, True, 0),    # more sequences than a wave's 64 lanes
 ])
 def test_decode_matches_dequantised_oracle(B, Hq, Hkv, Nq, d, lo, hi, causal, splits):
     dev = need_gpu()
